@@ -1,0 +1,159 @@
+/*
+ * mi.h - C ABI of libmi.so: attention-state merging and split-KV paged decode
+ * on AMD MI355X (gfx950).
+ *
+ * An attention state is a pair (v, s) for one query over a subset of keys:
+ * v[D] is the softmax-normalised output over that subset and s is the subset's
+ * log-sum-exp of scores in base 2 (s = natural LSE * log2(e)). States over
+ * disjoint key subsets merge exactly; the merge is commutative and associative
+ * ("F2 hints: merge_state, base-2 LSE merge", sections 1 and 2).
+ *
+ * Conventions shared by every entry point:
+ *  - Empty state: s = -inf, v = 0 (same page, section 5). Merging only empty
+ *    states yields s = -inf and v = 0, never NaN.
+ *  - Every s read by a merge is sanitised first: NaN and +inf count as -inf,
+ *    i.e. "no weight" ("FlashAttention's empty-row LSE", section 2.2). A state
+ *    with zero weight contributes nothing, even if its v holds NaN.
+ *  - s / lse values are always fp32, base 2.
+ *  - Arithmetic is fp32 with exp2/log2; v outputs are rounded to nearest even
+ *    into the requested dtype.
+ *  - Pointers are device pointers unless a name ends in _host. Every pointer is
+ *    borrowed: the caller allocates and frees; the library never allocates,
+ *    frees or synchronises and keeps no state between calls.
+ *  - stream is a hipStream_t passed as void*; NULL is the default stream.
+ *    Calls enqueue work and return; device faults surface at the caller's next
+ *    synchronisation.
+ *  - Arguments are validated on the host before anything is enqueued. A
+ *    non-MI_OK status means nothing was enqueued (except MI_ERR_HIP, returned
+ *    when a launch itself fails).
+ *  - Every output element is written, including those of empty rows and empty
+ *    splits.
+ *  - Tensors are dense and row-major ("C order") in the shapes given below.
+ *    16-bit and fp32 tensors must be 16-byte aligned.
+ */
+#ifndef MI_H_
+#define MI_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MI_F16 = 0, MI_BF16 = 1, MI_F32 = 2 } mi_dtype;
+
+typedef enum {
+  MI_OK = 0,
+  MI_ERR_NULL = 1,        /* a required pointer is NULL */
+  MI_ERR_SHAPE = 2,       /* a size is negative/zero where it must be positive, or inconsistent */
+  MI_ERR_DTYPE = 3,       /* dtype code out of range or not allowed for this argument */
+  MI_ERR_UNSUPPORTED = 4, /* valid but not built: head dim, page size, group size, alignment */
+  MI_ERR_HIP = 5,         /* a HIP launch failed */
+  MI_ERR_ALIAS = 6        /* outputs overlap inputs other than by exact in-place aliasing */
+} mi_status;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* mi_status_string(mi_status status);
+
+/*
+ * Merge two states per row ("F2 hints: merge_state, base-2 LSE merge",
+ * section 3; empty states, section 5).
+ *   v_a, v_b : [S, H, D] of v_dtype        s_a, s_b : [S, H] fp32, base 2
+ *   v_out    : [S, H, D] of out_dtype      s_out    : [S, H] fp32 (may be NULL)
+ * For each row r = pos*H + h: m = max(s_a, s_b); w = 2^(s - m) (0 for an
+ * empty state); v = (w_a v_a + w_b v_b) / (w_a + w_b); s = m + log2(w_a + w_b).
+ * In-place use is allowed: v_out may equal v_a or v_b when out_dtype ==
+ * v_dtype, and s_out may equal s_a or s_b. Any other overlap is MI_ERR_ALIAS.
+ * S == 0 is a no-op. D must be a positive multiple of 8, at most 512.
+ */
+mi_status mi_merge_state(const void* v_a, const float* s_a, const void* v_b, const float* s_b,
+                         void* v_out, float* s_out, int64_t S, int32_t H, int32_t D,
+                         mi_dtype v_dtype, mi_dtype out_dtype, void* stream);
+
+/*
+ * Merge N states per (pos, h) ("F2 hints: merge_state, base-2 LSE merge",
+ * section 4): the N states sit between position and head.
+ *   v     : [S, N, H, D] of v_dtype      s     : [S, N, H] fp32, base 2
+ *   v_out : [S, H, D] of out_dtype       s_out : [S, H] fp32 (may be NULL)
+ * s[pos, n, h] is at flat offset (pos*N + n)*H + h. The result is the merge of
+ * the N states; N == 1 sanitises and copies. Used with fp32 v, H = 1 and
+ * S = B*Hq it is the combine of split-KV decode ("L3 hints: split-KV decode and
+ * LSE merge", section 3). Outputs must not overlap inputs. S == 0 is a no-op.
+ * D must be a positive multiple of 8, at most 512.
+ */
+mi_status mi_merge_states(const void* v, const float* s, void* v_out, float* s_out, int64_t S,
+                          int32_t N, int32_t H, int32_t D, mi_dtype v_dtype, mi_dtype out_dtype,
+                          void* stream);
+
+/*
+ * Choose the number of KV splits for one decode step ("L3 hints: split-KV
+ * decode and LSE merge", section 6: make B*Hkv*splits a few times the compute
+ * unit count while each split keeps several pages; do not split when B*Hkv is
+ * already large). Host only; ctx_lens_host is a HOST array of B lengths.
+ * Rule: the smallest of {1, 4, 16, 64} with B*Hkv*splits >= 2*num_cus (64 if
+ * none), then step down through the set while the longest sequence would give
+ * a split fewer than 8 pages. Writes the choice to *num_splits_out.
+ * num_cus <= 0 asks the current HIP device for its compute unit count.
+ */
+mi_status mi_plan_splits(int32_t B, int32_t Hkv, const int32_t* ctx_lens_host, int32_t page_size,
+                         int32_t num_cus, int32_t* num_splits_out);
+
+/*
+ * Page range [*p_start, *p_end) of split `split` for a sequence of ctx tokens
+ * ("L3 hints: split-KV decode and LSE merge", section 2):
+ *   num_pages = ceil(ctx / page_size); per = ceil(num_pages / num_splits);
+ *   p_start = split * per; p_end = min(p_start + per, num_pages).
+ * The split is empty when p_end <= p_start. Host only; the decode kernels use
+ * the same formula on the device.
+ */
+mi_status mi_split_range(int32_t ctx, int32_t page_size, int32_t num_splits, int32_t split,
+                         int32_t* p_start, int32_t* p_end);
+
+/*
+ * Split-KV paged decode, pass 1 only (Flash-Decoding's producer, "L3 hints:
+ * split-KV decode and LSE merge", sections 1-5): one workgroup per
+ * (split, kv head, sequence) runs an online softmax over its split's pages and
+ * writes that split's normalised output and base-2 LSE. An empty split writes
+ * o = 0, lse = -inf.
+ *   q          : [B, Hq, D] of kv_dtype (one new token per sequence)
+ *   k_cache,
+ *   v_cache    : [num_phys_pages, Hkv, page_size, D] of kv_dtype
+ *   page_table : [B, pt_stride] int32, logical page -> physical page
+ *   ctx_lens   : [B] int32 (device) tokens per sequence
+ *   o_part     : [B, Hq, num_splits, D] fp32   lse_part : [B, Hq, num_splits] fp32
+ * Query head hq reads kv head hq / (Hq / Hkv). Scores are sm_scale * q.k.
+ * Device data is clamped, never trusted: a negative ctx counts as 0, at most
+ * pt_stride pages of a sequence are read, and a page id outside
+ * [0, num_phys_pages) contributes no tokens. Token slots at or past ctx are
+ * never used, whatever they hold. Supported: D = 128, page_size = 16,
+ * Hq / Hkv in {1, 2, 4, 8}, kv_dtype f16 or bf16, num_splits in [1, 1024].
+ */
+mi_status mi_split_kv_partial(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* page_table, int32_t pt_stride,
+                              const int32_t* ctx_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                              int32_t D, int32_t page_size, int64_t num_phys_pages,
+                              int32_t num_splits, float sm_scale, mi_dtype kv_dtype,
+                              float* o_part, float* lse_part, void* stream);
+
+/*
+ * Split-KV paged decode, both passes ("L3 hints: split-KV decode and LSE
+ * merge", section 1): mi_split_kv_partial followed by the combine, i.e.
+ * mi_merge_states over o_part viewed as [B*Hq, num_splits, 1, D], on `stream`.
+ * o_part / lse_part are caller-owned fp32 workspaces (shapes as above) and are
+ * left holding the partials. Outputs: o [B, Hq, D] of out_dtype, and
+ * lse [B, Hq] fp32 base 2 (may be NULL). A sequence with ctx = 0 gets
+ * o = 0, lse = -inf.
+ */
+mi_status mi_split_kv_decode(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* page_table, int32_t pt_stride, const int32_t* ctx_lens,
+                             int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size,
+                             int64_t num_phys_pages, int32_t num_splits, float sm_scale,
+                             mi_dtype kv_dtype, float* o_part, float* lse_part, void* o,
+                             float* lse, mi_dtype out_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI_H_ */

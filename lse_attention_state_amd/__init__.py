@@ -1,1 +1,216 @@
-"""placeholder"""
+"""Python binding for libmi.so: attention-state merging and split-KV decode on MI355X.
+
+The functions below only marshal arguments: they check tensor dtypes, shapes,
+devices and contiguity, allocate missing outputs with torch (device memory is
+plumbing), and call the C ABI declared in ``include/mi.h`` on the current
+torch stream. Every step of the computation runs in the HIP kernels of
+libmi.so. There is no CPU fallback: if the library is missing or fails to
+load, every call raises.
+
+Conventions (see ``include/mi.h``): an attention state is (v, s) with s the
+base-2 log-sum-exp, empty = (0, -inf); s / lse tensors are float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmi.so")
+
+MI_F16, MI_BF16, MI_F32 = 0, 1, 2
+_DT = {torch.float16: MI_F16, torch.bfloat16: MI_BF16, torch.float32: MI_F32}
+
+STATUS = {0: "MI_OK", 1: "MI_ERR_NULL", 2: "MI_ERR_SHAPE", 3: "MI_ERR_DTYPE",
+          4: "MI_ERR_UNSUPPORTED", 5: "MI_ERR_HIP", 6: "MI_ERR_ALIAS"}
+
+# (name, argtypes) of every exported entry point; the list mirrors include/mi.h.
+_P, _I32, _I64, _F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+SIGNATURES = {
+    "mi_status_string": [ctypes.c_int],
+    "mi_merge_state": [_P, _P, _P, _P, _P, _P, _I64, _I32, _I32, ctypes.c_int, ctypes.c_int, _P],
+    "mi_merge_states": [_P, _P, _P, _P, _I64, _I32, _I32, _I32, ctypes.c_int, ctypes.c_int, _P],
+    "mi_plan_splits": [_I32, _I32, _P, _I32, _I32, _P],
+    "mi_split_range": [_I32, _I32, _I32, _I32, _P, _P],
+    "mi_split_kv_partial": [_P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I64, _I32,
+                            _F, ctypes.c_int, _P, _P, _P],
+    "mi_split_kv_decode": [_P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I64, _I32, _F,
+                           ctypes.c_int, _P, _P, _P, _P, ctypes.c_int, _P],
+}
+
+
+class MiError(RuntimeError):
+    def __init__(self, name: str, status: int):
+        super().__init__(f"{name} failed: {STATUS.get(status, status)}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmi.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with `python -m lse_attention_state_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, argtypes in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.argtypes = argtypes
+            fn.restype = ctypes.c_char_p if name == "mi_status_string" else ctypes.c_int
+        _lib = handle
+    return _lib
+
+
+def _call(name: str, *args):
+    rc = getattr(lib(), name)(*args)
+    if rc != 0:
+        raise MiError(name, rc)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _check_cuda(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _f32(t, name):
+    if t is not None and t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32")
+
+
+# ----------------------------------------------------------------------------- merges
+
+def merge_state(v_a, s_a, v_b, s_b, out_dtype=None, v_out=None, s_out=None, return_s=True):
+    """Merge two states: v_* [..., D], s_* [...] (float32, base 2). Returns (v, s).
+
+    ``v_out`` may be ``v_a`` or ``v_b`` (in place) when dtypes match; ``s_out``
+    may be ``s_a`` or ``s_b``."""
+    _check_cuda(v_a, s_a, v_b, s_b, v_out, s_out)
+    _f32(s_a, "s_a"), _f32(s_b, "s_b"), _f32(s_out, "s_out")
+    if v_a.shape != v_b.shape or s_a.shape != s_b.shape or v_a.shape[:-1] != s_a.shape:
+        raise ValueError("merge_state: shapes must be v [..., D] and s [...] for both states")
+    out_dtype = out_dtype or (v_out.dtype if v_out is not None else v_a.dtype)
+    if v_out is None:
+        v_out = torch.empty(v_a.shape, dtype=out_dtype, device=v_a.device)
+    if s_out is None and return_s:
+        s_out = torch.empty(s_a.shape, dtype=torch.float32, device=v_a.device)
+    D = v_a.shape[-1]
+    rows = s_a.numel()
+    _call("mi_merge_state", _ptr(v_a), _ptr(s_a), _ptr(v_b), _ptr(s_b), _ptr(v_out), _ptr(s_out),
+          rows, 1, D, _dt(v_a), _dt(v_out), _stream(v_a))
+    return v_out, s_out
+
+
+def merge_states(v, s, out_dtype=None, v_out=None, s_out=None, return_s=True):
+    """Merge N states: v [S, N, H, D], s [S, N, H] -> (v [S, H, D], s [S, H])."""
+    _check_cuda(v, s, v_out, s_out)
+    _f32(s, "s"), _f32(s_out, "s_out")
+    if v.dim() != 4 or s.shape != v.shape[:3]:
+        raise ValueError("merge_states: v must be [S, N, H, D] and s [S, N, H]")
+    S, N, H, D = v.shape
+    out_dtype = out_dtype or (v_out.dtype if v_out is not None else v.dtype)
+    if v_out is None:
+        v_out = torch.empty((S, H, D), dtype=out_dtype, device=v.device)
+    if s_out is None and return_s:
+        s_out = torch.empty((S, H), dtype=torch.float32, device=v.device)
+    _call("mi_merge_states", _ptr(v), _ptr(s), _ptr(v_out), _ptr(s_out), S, N, H, D, _dt(v),
+          _dt(v_out), _stream(v))
+    return v_out, s_out
+
+
+# ----------------------------------------------------------------------------- planning
+
+def plan_splits(ctx_lens, Hkv: int, page_size: int = 16, num_cus: int = 0) -> int:
+    """Split count for a decode step; ``ctx_lens`` is host data (list / numpy / CPU tensor)."""
+    import numpy as np
+    ctx = np.ascontiguousarray(np.asarray(ctx_lens.cpu() if isinstance(ctx_lens, torch.Tensor)
+                                          else ctx_lens, dtype=np.int32))
+    out = ctypes.c_int32()
+    _call("mi_plan_splits", len(ctx), Hkv, ctx.ctypes.data_as(ctypes.c_void_p), page_size,
+          num_cus, ctypes.byref(out))
+    return out.value
+
+
+def split_range(ctx: int, page_size: int, num_splits: int, split: int):
+    a, b = ctypes.c_int32(), ctypes.c_int32()
+    _call("mi_split_range", ctx, page_size, num_splits, split, ctypes.byref(a), ctypes.byref(b))
+    return a.value, b.value
+
+
+# ----------------------------------------------------------------------------- decode
+
+def _decode_args(q, k_cache, v_cache, page_table, ctx_lens):
+    _check_cuda(q, k_cache, v_cache, page_table, ctx_lens)
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q must be [B, Hq, D] and k/v caches [pages, Hkv, PAGE, D]")
+    if q.dtype != k_cache.dtype or k_cache.dtype != v_cache.dtype:
+        raise TypeError("q, k_cache and v_cache must share one dtype")
+    if page_table.dtype != torch.int32 or ctx_lens.dtype != torch.int32:
+        raise TypeError("page_table and ctx_lens must be int32")
+    B, Hq, D = q.shape
+    P, Hkv, page, Dk = k_cache.shape
+    if Dk != D or page_table.dim() != 2 or page_table.shape[0] != B or ctx_lens.shape != (B,):
+        raise ValueError("inconsistent decode shapes")
+    return B, Hq, Hkv, D, page, P
+
+
+def split_kv_partial(q, k_cache, v_cache, page_table, ctx_lens, num_splits: int, sm_scale: float,
+                     o_part=None, lse_part=None):
+    """Pass 1 only -> (o_part [B, Hq, splits, D] f32, lse_part [B, Hq, splits] f32)."""
+    B, Hq, Hkv, D, page, P = _decode_args(q, k_cache, v_cache, page_table, ctx_lens)
+    if o_part is None:
+        o_part = torch.empty((B, Hq, num_splits, D), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((B, Hq, num_splits), dtype=torch.float32, device=q.device)
+    _check_cuda(o_part, lse_part)
+    _call("mi_split_kv_partial", _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+          page_table.shape[1], _ptr(ctx_lens), B, Hq, Hkv, D, page, P, num_splits,
+          float(sm_scale), _dt(q), _ptr(o_part), _ptr(lse_part), _stream(q))
+    return o_part, lse_part
+
+
+def split_kv_decode(q, k_cache, v_cache, page_table, ctx_lens, num_splits: int, sm_scale: float,
+                    out_dtype=None, o_part=None, lse_part=None, out=None, lse=None,
+                    return_lse=True, return_partials=False):
+    """Both passes -> (o [B, Hq, D], lse [B, Hq] f32 base 2[, o_part, lse_part])."""
+    B, Hq, Hkv, D, page, P = _decode_args(q, k_cache, v_cache, page_table, ctx_lens)
+    out_dtype = out_dtype or (out.dtype if out is not None else q.dtype)
+    if o_part is None:
+        o_part = torch.empty((B, Hq, num_splits, D), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((B, Hq, num_splits), dtype=torch.float32, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check_cuda(o_part, lse_part, out, lse)
+    _call("mi_split_kv_decode", _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+          page_table.shape[1], _ptr(ctx_lens), B, Hq, Hkv, D, page, P, num_splits,
+          float(sm_scale), _dt(q), _ptr(o_part), _ptr(lse_part), _ptr(out), _ptr(lse),
+          _dt(out), _stream(q))
+    if return_partials:
+        return out, lse, o_part, lse_part
+    return out, lse

@@ -1,0 +1,262 @@
+// C ABI of libmi.so: argument validation on the host, then kernel launches on
+// the caller's stream. Nothing is allocated, freed or synchronised here.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "launch.h"
+#include "mi.h"
+#include "split_range.h"
+
+namespace {
+
+bool dtype_ok(int dt) { return dt == MI_F16 || dt == MI_BF16 || dt == MI_F32; }
+
+int64_t dtype_bytes(int dt) { return dt == MI_F32 ? 4 : 2; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Byte ranges [p, p + n) and [q, q + m) share a byte.
+bool overlaps(const void* p, int64_t n, const void* q, int64_t m) {
+  if (p == nullptr || q == nullptr || n <= 0 || m <= 0) return false;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  const uintptr_t b = reinterpret_cast<uintptr_t>(q);
+  return a < b + static_cast<uintptr_t>(m) && b < a + static_cast<uintptr_t>(n);
+}
+
+// An output may coincide exactly with one input (in-place) when `exact_ok`;
+// any other shared byte is an aliasing error.
+bool bad_alias(const void* out, int64_t out_bytes, const void* in, int64_t in_bytes, bool exact_ok) {
+  if (!overlaps(out, out_bytes, in, in_bytes)) return false;
+  return !(exact_ok && out == in && out_bytes == in_bytes);
+}
+
+mi_status from_hip(hipError_t e) { return e == hipSuccess ? MI_OK : MI_ERR_HIP; }
+
+// Products of validated non-negative sizes stay below 2^62 bytes.
+bool size_ok(int64_t a, int64_t b, int64_t c = 1, int64_t d = 1) {
+  const int64_t lim = int64_t(1) << 62;
+  int64_t x = a;
+  for (int64_t f : {b, c, d}) {
+    if (f != 0 && x > lim / f) return false;
+    x *= f;
+  }
+  return true;
+}
+
+mi_status check_merge_dims(int32_t H, int32_t D, int dt_in, int dt_out) {
+  if (H <= 0 || D <= 0) return MI_ERR_SHAPE;
+  if (!dtype_ok(dt_in) || !dtype_ok(dt_out)) return MI_ERR_DTYPE;
+  if (D % 8 != 0 || D > 512) return MI_ERR_UNSUPPORTED;
+  return MI_OK;
+}
+
+struct DecodeShape {
+  int64_t q_bytes, cache_bytes, pt_bytes, ctx_bytes, opart_bytes, lpart_bytes;
+};
+
+mi_status check_decode(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* page_table, int32_t pt_stride, const int32_t* ctx_lens,
+                       int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size,
+                       int64_t num_phys_pages, int32_t num_splits, mi_dtype kv_dtype,
+                       const float* o_part, const float* lse_part, DecodeShape* shp) {
+  if (!q || !k_cache || !v_cache || !page_table || !ctx_lens || !o_part || !lse_part)
+    return MI_ERR_NULL;
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || page_size <= 0 || pt_stride <= 0 ||
+      num_phys_pages <= 0 || num_splits <= 0 || Hq % Hkv != 0)
+    return MI_ERR_SHAPE;
+  if (kv_dtype != MI_F16 && kv_dtype != MI_BF16) return MI_ERR_DTYPE;
+  const int G = Hq / Hkv;
+  if (D != 128 || page_size != 16 || !(G == 1 || G == 2 || G == 4 || G == 8) ||
+      num_splits > 1024 || B > 65535 || Hkv > 65535)
+    return MI_ERR_UNSUPPORTED;
+  if (!size_ok(num_phys_pages, Hkv, static_cast<int64_t>(page_size) * D, 2) ||
+      !size_ok(B, Hq, num_splits, D * 4) || !size_ok(B, pt_stride, 4))
+    return MI_ERR_SHAPE;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(o_part, 16) || !aligned(lse_part, 4) || !aligned(page_table, 4) ||
+      !aligned(ctx_lens, 4))
+    return MI_ERR_UNSUPPORTED;
+  shp->q_bytes = int64_t(B) * Hq * D * 2;
+  shp->cache_bytes = num_phys_pages * Hkv * page_size * D * 2;
+  shp->pt_bytes = int64_t(B) * pt_stride * 4;
+  shp->ctx_bytes = int64_t(B) * 4;
+  shp->opart_bytes = int64_t(B) * Hq * num_splits * D * 4;
+  shp->lpart_bytes = int64_t(B) * Hq * num_splits * 4;
+  const void* ins[5] = {q, k_cache, v_cache, page_table, ctx_lens};
+  const int64_t in_bytes[5] = {shp->q_bytes, shp->cache_bytes, shp->cache_bytes, shp->pt_bytes,
+                               shp->ctx_bytes};
+  for (int i = 0; i < 5; ++i) {
+    if (overlaps(o_part, shp->opart_bytes, ins[i], in_bytes[i]) ||
+        overlaps(lse_part, shp->lpart_bytes, ins[i], in_bytes[i]))
+      return MI_ERR_ALIAS;
+  }
+  if (overlaps(o_part, shp->opart_bytes, lse_part, shp->lpart_bytes)) return MI_ERR_ALIAS;
+  return MI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mi_status_string(mi_status status) {
+  switch (status) {
+    case MI_OK: return "MI_OK";
+    case MI_ERR_NULL: return "MI_ERR_NULL: a required pointer is NULL";
+    case MI_ERR_SHAPE: return "MI_ERR_SHAPE: invalid or inconsistent size";
+    case MI_ERR_DTYPE: return "MI_ERR_DTYPE: dtype not allowed for this argument";
+    case MI_ERR_UNSUPPORTED: return "MI_ERR_UNSUPPORTED: size, dtype or alignment not supported";
+    case MI_ERR_HIP: return "MI_ERR_HIP: a HIP call failed";
+    case MI_ERR_ALIAS: return "MI_ERR_ALIAS: outputs overlap inputs";
+  }
+  return "unknown mi_status";
+}
+
+mi_status mi_merge_state(const void* v_a, const float* s_a, const void* v_b, const float* s_b,
+                         void* v_out, float* s_out, int64_t S, int32_t H, int32_t D,
+                         mi_dtype v_dtype, mi_dtype out_dtype, void* stream) {
+  if (!v_a || !s_a || !v_b || !s_b || !v_out) return MI_ERR_NULL;
+  if (S < 0) return MI_ERR_SHAPE;
+  mi_status st = check_merge_dims(H, D, v_dtype, out_dtype);
+  if (st != MI_OK) return st;
+  if (!size_ok(S, H, D, 4)) return MI_ERR_SHAPE;
+  if (!aligned(v_a, 16) || !aligned(v_b, 16) || !aligned(v_out, 16) || !aligned(s_a, 4) ||
+      !aligned(s_b, 4) || !aligned(s_out, 4))
+    return MI_ERR_UNSUPPORTED;
+  const int64_t rows = S * H;
+  const int64_t in_b = rows * D * dtype_bytes(v_dtype);
+  const int64_t out_b = rows * D * dtype_bytes(out_dtype);
+  const int64_t s_b_bytes = rows * 4;
+  const bool same_dt = v_dtype == out_dtype;
+  if (bad_alias(v_out, out_b, v_a, in_b, same_dt) || bad_alias(v_out, out_b, v_b, in_b, same_dt) ||
+      overlaps(v_out, out_b, s_a, s_b_bytes) || overlaps(v_out, out_b, s_b, s_b_bytes) ||
+      bad_alias(s_out, s_b_bytes, s_a, s_b_bytes, true) ||
+      bad_alias(s_out, s_b_bytes, s_b, s_b_bytes, true) ||
+      overlaps(s_out, s_b_bytes, v_a, in_b) || overlaps(s_out, s_b_bytes, v_b, in_b) ||
+      overlaps(s_out, s_b_bytes, v_out, out_b))
+    return MI_ERR_ALIAS;
+  if (rows == 0) return MI_OK;
+  return from_hip(mi::launch_merge_state(v_a, s_a, v_b, s_b, v_out, s_out, rows, D, v_dtype,
+                                         out_dtype, static_cast<hipStream_t>(stream)));
+}
+
+mi_status mi_merge_states(const void* v, const float* s, void* v_out, float* s_out, int64_t S,
+                          int32_t N, int32_t H, int32_t D, mi_dtype v_dtype, mi_dtype out_dtype,
+                          void* stream) {
+  if (!v || !s || !v_out) return MI_ERR_NULL;
+  if (S < 0 || N <= 0) return MI_ERR_SHAPE;
+  mi_status st = check_merge_dims(H, D, v_dtype, out_dtype);
+  if (st != MI_OK) return st;
+  if (!size_ok(S, N, H, static_cast<int64_t>(D) * 4)) return MI_ERR_SHAPE;
+  if (!aligned(v, 16) || !aligned(v_out, 16) || !aligned(s, 4) || !aligned(s_out, 4))
+    return MI_ERR_UNSUPPORTED;
+  const int64_t in_v = S * N * H * D * dtype_bytes(v_dtype);
+  const int64_t in_s = S * N * H * 4;
+  const int64_t out_v = S * H * D * dtype_bytes(out_dtype);
+  const int64_t out_s = S * H * 4;
+  if (overlaps(v_out, out_v, v, in_v) || overlaps(v_out, out_v, s, in_s) ||
+      overlaps(s_out, out_s, v, in_v) || overlaps(s_out, out_s, s, in_s) ||
+      overlaps(s_out, out_s, v_out, out_v))
+    return MI_ERR_ALIAS;
+  if (S == 0) return MI_OK;
+  return from_hip(mi::launch_merge_states(v, s, v_out, s_out, S, N, H, D, v_dtype, out_dtype,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+mi_status mi_split_range(int32_t ctx, int32_t page_size, int32_t num_splits, int32_t split,
+                         int32_t* p_start, int32_t* p_end) {
+  if (!p_start || !p_end) return MI_ERR_NULL;
+  if (ctx < 0 || page_size <= 0 || num_splits <= 0 || split < 0 || split >= num_splits)
+    return MI_ERR_SHAPE;
+  int a, b;
+  mi::split_pages(ctx, page_size, num_splits, split, &a, &b);
+  *p_start = a;
+  *p_end = b;
+  return MI_OK;
+}
+
+mi_status mi_plan_splits(int32_t B, int32_t Hkv, const int32_t* ctx_lens_host, int32_t page_size,
+                         int32_t num_cus, int32_t* num_splits_out) {
+  if (!ctx_lens_host || !num_splits_out) return MI_ERR_NULL;
+  if (B <= 0 || Hkv <= 0 || page_size <= 0) return MI_ERR_SHAPE;
+  int max_pages = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    if (ctx_lens_host[b] < 0) return MI_ERR_SHAPE;
+    const int np = mi::ceil_div(ctx_lens_host[b], page_size);
+    if (np > max_pages) max_pages = np;
+  }
+  if (num_cus <= 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        num_cus <= 0)
+      return MI_ERR_HIP;
+  }
+  // "L3 hints", section 6: enough workgroups to fill the device a few times
+  // over (here: twice the compute units), but no split thinner than 8 pages.
+  static const int kChoices[4] = {1, 4, 16, 64};
+  int pick = 3;
+  for (int i = 0; i < 4; ++i) {
+    if (int64_t(B) * Hkv * kChoices[i] >= 2 * int64_t(num_cus)) {
+      pick = i;
+      break;
+    }
+  }
+  while (pick > 0 && mi::ceil_div(max_pages, kChoices[pick]) < 8) --pick;
+  *num_splits_out = kChoices[pick];
+  return MI_OK;
+}
+
+mi_status mi_split_kv_partial(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* page_table, int32_t pt_stride,
+                              const int32_t* ctx_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                              int32_t D, int32_t page_size, int64_t num_phys_pages,
+                              int32_t num_splits, float sm_scale, mi_dtype kv_dtype,
+                              float* o_part, float* lse_part, void* stream) {
+  DecodeShape shp;
+  mi_status st = check_decode(q, k_cache, v_cache, page_table, pt_stride, ctx_lens, B, Hq, Hkv, D,
+                              page_size, num_phys_pages, num_splits, kv_dtype, o_part, lse_part,
+                              &shp);
+  if (st != MI_OK) return st;
+  if (B == 0) return MI_OK;
+  return from_hip(mi::launch_split_kv_partial(q, k_cache, v_cache, page_table, pt_stride, ctx_lens,
+                                              B, Hq, Hkv, num_phys_pages, num_splits, sm_scale,
+                                              kv_dtype, o_part, lse_part,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+mi_status mi_split_kv_decode(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* page_table, int32_t pt_stride, const int32_t* ctx_lens,
+                             int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size,
+                             int64_t num_phys_pages, int32_t num_splits, float sm_scale,
+                             mi_dtype kv_dtype, float* o_part, float* lse_part, void* o,
+                             float* lse, mi_dtype out_dtype, void* stream) {
+  if (!o) return MI_ERR_NULL;
+  DecodeShape shp;
+  mi_status st = check_decode(q, k_cache, v_cache, page_table, pt_stride, ctx_lens, B, Hq, Hkv, D,
+                              page_size, num_phys_pages, num_splits, kv_dtype, o_part, lse_part,
+                              &shp);
+  if (st != MI_OK) return st;
+  if (!dtype_ok(out_dtype)) return MI_ERR_DTYPE;
+  if (!aligned(o, 16) || !aligned(lse, 4)) return MI_ERR_UNSUPPORTED;
+  const int64_t o_bytes = int64_t(B) * Hq * D * dtype_bytes(out_dtype);
+  const int64_t lse_bytes = int64_t(B) * Hq * 4;
+  const void* all[7] = {q, k_cache, v_cache, page_table, ctx_lens, o_part, lse_part};
+  const int64_t all_b[7] = {shp.q_bytes, shp.cache_bytes, shp.cache_bytes, shp.pt_bytes,
+                            shp.ctx_bytes, shp.opart_bytes, shp.lpart_bytes};
+  for (int i = 0; i < 7; ++i)
+    if (overlaps(o, o_bytes, all[i], all_b[i]) || overlaps(lse, lse_bytes, all[i], all_b[i]))
+      return MI_ERR_ALIAS;
+  if (overlaps(o, o_bytes, lse, lse_bytes)) return MI_ERR_ALIAS;
+  if (B == 0) return MI_OK;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = mi::launch_split_kv_partial(q, k_cache, v_cache, page_table, pt_stride, ctx_lens,
+                                             B, Hq, Hkv, num_phys_pages, num_splits, sm_scale,
+                                             kv_dtype, o_part, lse_part, s);
+  if (e != hipSuccess) return MI_ERR_HIP;
+  // The combine: o_part [B, Hq, splits, D] is merge_states' [S = B*Hq, N = splits, H = 1, D].
+  return from_hip(mi::launch_merge_states(o_part, lse_part, o, lse, int64_t(B) * Hq, num_splits,
+                                          1, D, MI_F32, out_dtype, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,317 @@
+// Split-KV paged decode, pass 1, for gfx950 ("L3 hints: split-KV decode and
+// LSE merge", sections 1-5; Flash-Decoding's producer).
+//
+// One workgroup per (split, kv head, sequence). The split's pages come from
+// the page-range formula; each page of the paged cache holds, per kv head, a
+// contiguous [PAGE=16, D=128] tile (4 KiB in fp16/bf16).
+//
+// Work mapping inside the workgroup (4 waves, 256 lanes):
+//  - wave w owns token slots 4w..4w+3 of every page; within a wave, lane l
+//    owns slot 4w + l/16 and the 8-element chunk (l%16)*8 of D. A wave's
+//    quarter of a K or V tile is one contiguous KiB, read with a single fully
+//    coalesced 16-byte-per-lane load.
+//  - all G = Hq/Hkv query heads of the kv head are served from the same loaded
+//    tile (GQA reuse): q.k partial dots use v_dot2 (fp16/bf16 pairs into fp32),
+//    and a 16-lane DPP reduction completes each score.
+//  - every 16-lane row is its own online-softmax stream (m, l, acc) in base 2:
+//    the softmax scale is multiplied by log2(e) once on the host, so weights
+//    are the hardware exp2. Streams are merged at the end with the state merge
+//    (wave-internal cross-lane, then across waves through LDS).
+//  - pages are software-pipelined: each wave keeps kDepth pages of K and V in
+//    flight in registers while it computes on earlier ones; the physical page
+//    ids come from the page table through the scalar cache.
+//
+// Guards: the running max is replaced by 0 when it is -inf before it is
+// subtracted ("FlashAttention's empty-row LSE", section 2.3), so fully masked
+// streams never form -inf - (-inf). Token slots at or past ctx are excluded by
+// select on both the score and the value, so whatever they hold (even NaN)
+// cannot leak. An empty split writes o = 0 and lse = -inf ("L3 hints",
+// section 4).
+#include "common.h"
+#include "launch.h"
+#include "split_range.h"
+
+#include <type_traits>
+
+namespace mi {
+namespace {
+
+constexpr int kD = 128;
+constexpr int kPage = 16;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kDepth = 8;
+static_assert(64 % kDepth == 0, "page-id chunks hold whole prefetch batches");
+constexpr float kRescaleSlack = 8.0f;
+// Word 3 of a gfx9 buffer descriptor for raw (untyped, unswizzled) access.
+constexpr int kBufferFlags = 0x00020000;
+
+template <int DT>
+__device__ __forceinline__ float dot8(const u32x4_t& q, const u32x4_t& k) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (DT == MI_F16)
+      acc = __builtin_amdgcn_fdot2(as_half2(q[i]), as_half2(k[i]), acc, false);
+    else
+      acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf162(q[i]), as_bf162(k[i]), acc, false);
+  }
+  return acc;
+}
+
+template <int DT>
+__device__ __forceinline__ void unpack8(const u32x4_t& w, float (&x)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (DT == MI_F16) {
+      x[2 * i] = f16_lo(w[i]);
+      x[2 * i + 1] = f16_hi(w[i]);
+    } else {
+      x[2 * i] = bf16_lo(w[i]);
+      x[2 * i + 1] = bf16_hi(w[i]);
+    }
+  }
+}
+
+template <int DT, int G>
+__global__ __launch_bounds__(kThreads) void split_kv_partial_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, const int32_t* __restrict__ page_table, int pt_stride,
+    const int32_t* __restrict__ ctx_lens, int Hkv, int64_t num_phys, int num_splits,
+    float qk_scale_log2, float* __restrict__ o_part, float* __restrict__ lse_part) {
+  __shared__ float lds_acc[kWaves][G][kD];
+  __shared__ float lds_ml[kWaves][G][2];
+
+  const int split = blockIdx.x;
+  const int hkv = blockIdx.y;
+  const int b = blockIdx.z;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int slot = wave * 4 + (lane >> 4);
+  const int d0 = (lane & 15) * 8;
+  const int Hq = Hkv * G;
+
+  // Device lengths are clamped: negative -> 0, at most pt_stride pages.
+  int64_t ctx64 = ctx_lens[b];
+  ctx64 = ctx64 < 0 ? 0 : ctx64;
+  const int64_t cap = static_cast<int64_t>(pt_stride) * kPage;
+  const int ctx = static_cast<int>(ctx64 < cap ? ctx64 : cap);
+  int p0, p1;
+  split_pages(ctx, kPage, num_splits, split, &p0, &p1);
+  const int npages = p1 > p0 ? p1 - p0 : 0;
+
+  u32x4_t qw[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    qw[h] = *reinterpret_cast<const u32x4_t*>(q + (static_cast<int64_t>(b) * Hq + hkv * G + h) * kD + d0);
+
+  float m[G], l[G], acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -kInf;
+    l[h] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[h][j] = 0.0f;
+  }
+
+  // Page ids: lane l holds the id of page (chunk*64 + l) of the split; the
+  // issuing code broadcasts them with readlane, off the memory critical path.
+  const int32_t* pt = page_table + static_cast<int64_t>(b) * pt_stride + p0;
+  auto load_ids = [&](int first) {
+    const int i = first + lane;
+    return pt[i < npages ? i : npages - 1];
+  };
+
+  // Each page's K and V tiles for this kv head are read through a buffer
+  // descriptor covering exactly that 4 KiB tile. Pages past the split's end,
+  // and page ids outside [0, num_phys), get a descriptor with no records: the
+  // hardware returns zeros for them without touching memory, so every
+  // prefetch below is unconditional.
+  const int lane_bytes = (wave * 64 + lane) * 16;
+  const int64_t tile_elems = static_cast<int64_t>(kPage) * kD;
+  u32x4_t kb[kDepth], vb[kDepth];
+  bool ok[kDepth];
+  int ids = 0;
+  auto issue = [&](int i, int j) {
+    const int32_t phys = __builtin_amdgcn_readlane(ids, i & 63);
+    ok[j] = i < npages && phys >= 0 && phys < num_phys;
+    const int64_t tile = (static_cast<int64_t>(ok[j] ? phys : 0) * Hkv + hkv) * tile_elems;
+    const int records = ok[j] ? static_cast<int>(tile_elems * 2) : 0;
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kc + tile), 0, records, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vc + tile), 0, records, kBufferFlags);
+    kb[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, lane_bytes, 0, 0));
+    vb[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, lane_bytes, 0, 0));
+  };
+
+  // Online softmax with a lazily updated reference max m[h]: exponentials are
+  // taken against m[h] and the accumulators are rescaled only when a score
+  // exceeds m[h] by more than kRescaleSlack (or on a stream's first token), so
+  // p <= 2^kRescaleSlack and the common step is one exp2 and 8 FMAs per head.
+  // The state (m, l, acc) stays exact: l and acc are always relative to m.
+  auto consume = [&](int i, int j, auto masked_tag) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
+    const bool valid = !kMasked || ((p0 + i) * kPage + slot < ctx);
+    const bool page_ok = ok[j];  // false: past the split or a bad page id (zeros were loaded)
+    float v[8];
+    unpack8<DT>(vb[j], v);
+    if constexpr (kMasked) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = valid ? v[e] : 0.0f;
+    }
+    float x[G];
+    bool need_any = false;
+    bool need[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      x[h] = row16_sum(dot8<DT>(qw[h], kb[j])) * qk_scale_log2;
+      if constexpr (kMasked) x[h] = valid ? x[h] : -kInf;
+      x[h] = page_ok ? x[h] : -kInf;
+      need[h] = x[h] > m[h] + kRescaleSlack;
+      need_any |= need[h];
+    }
+    if (__builtin_amdgcn_ballot_w64(need_any) != 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float alpha = need[h] ? __builtin_amdgcn_exp2f(m[h] - x[h]) : 1.0f;
+        m[h] = need[h] ? x[h] : m[h];
+        l[h] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mu = (m[h] == -kInf) ? 0.0f : m[h];
+      const float p = __builtin_amdgcn_exp2f(x[h] - mu);
+      l[h] += p;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] = __builtin_fmaf(p, v[e], acc[h][e]);
+    }
+  };
+  // The only page that can hold slots at or past ctx is the sequence's last.
+  const bool tail_partial = (ctx % kPage) != 0;
+  const int last_page = ctx / kPage;  // logical index of a partial last page
+
+  if (npages > 0) {
+    const int iters = (npages + kDepth - 1) / kDepth * kDepth;
+    ids = load_ids(0);
+#pragma unroll
+    for (int j = 0; j < kDepth; ++j) issue(j, j);
+    for (int base = 0; base < iters; base += kDepth) {
+      // Pages base+kDepth .. base+2*kDepth-1 are issued in this batch; they
+      // share one 64-page chunk of ids because kDepth divides 64.
+      if (((base + kDepth) & 63) == 0) ids = load_ids(base + kDepth);
+#pragma unroll
+      for (int j = 0; j < kDepth; ++j) {
+        const int i = base + j;
+        // Every slot is consumed on every path (a skipped consume would make
+        // the compiler drain all loads before the slot's registers are reused).
+        if (tail_partial && p0 + i == last_page)
+          consume(i, j, std::true_type{});
+        else
+          consume(i, j, std::false_type{});
+        issue(i + kDepth, j);
+      }
+    }
+  }
+
+  // Merge the four token rows of the wave (lanes l, l^16, l^32, l^48).
+#pragma unroll
+  for (int sh = 16; sh <= 32; sh <<= 1) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mo = shfl_xor(m[h], sh);
+      const float lo = shfl_xor(l[h], sh);
+      const float M = __builtin_fmaxf(m[h], mo);
+      const float ws = guarded_exp2(m[h] - M);
+      const float wo = guarded_exp2(mo - M);
+      l[h] = l[h] * ws + lo * wo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float ao = shfl_xor(acc[h][e], sh);
+        acc[h][e] = acc[h][e] * ws + ao * wo;
+      }
+      m[h] = M;
+    }
+  }
+
+  // Merge the waves through LDS; wave w finalises heads w, w+4, ...
+  if (lane < 16) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) lds_acc[wave][h][d0 + e] = acc[h][e];
+      if (lane == 0) {
+        lds_ml[wave][h][0] = m[h];
+        lds_ml[wave][h][1] = l[h];
+      }
+    }
+  }
+  __syncthreads();
+  for (int h = wave; h < G; h += kWaves) {
+    float M = -kInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = __builtin_fmaxf(M, lds_ml[w][h][0]);
+    float Z = 0.0f, o0 = 0.0f, o1 = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float ww = guarded_exp2(lds_ml[w][h][0] - M);
+      Z = __builtin_fmaf(ww, lds_ml[w][h][1], Z);
+      o0 = __builtin_fmaf(ww, lds_acc[w][h][2 * lane], o0);
+      o1 = __builtin_fmaf(ww, lds_acc[w][h][2 * lane + 1], o1);
+    }
+    const float inv = guarded_inv(Z);
+    const int64_t row = static_cast<int64_t>(b) * Hq + hkv * G + h;
+    float* out = o_part + (row * num_splits + split) * kD + 2 * lane;
+    *reinterpret_cast<float2*>(out) = make_float2(o0 * inv, o1 * inv);
+    if (lane == 0) lse_part[row * num_splits + split] = (Z > 0.0f) ? M + hw_log2(Z) : -kInf;
+  }
+}
+
+template <int DT>
+hipError_t launch_group(int G, dim3 grid, hipStream_t st, const void* q, const void* kc,
+                        const void* vc, const int32_t* pt, int pt_stride, const int32_t* ctx,
+                        int Hkv, int64_t num_phys, int num_splits, float scale, float* o_part,
+                        float* lse_part) {
+  const uint16_t* q16 = static_cast<const uint16_t*>(q);
+  const uint16_t* k16 = static_cast<const uint16_t*>(kc);
+  const uint16_t* v16 = static_cast<const uint16_t*>(vc);
+  switch (G) {
+    case 1:
+      split_kv_partial_kernel<DT, 1><<<grid, kThreads, 0, st>>>(q16, k16, v16, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part);
+      break;
+    case 2:
+      split_kv_partial_kernel<DT, 2><<<grid, kThreads, 0, st>>>(q16, k16, v16, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part);
+      break;
+    case 4:
+      split_kv_partial_kernel<DT, 4><<<grid, kThreads, 0, st>>>(q16, k16, v16, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part);
+      break;
+    default:
+      split_kv_partial_kernel<DT, 8><<<grid, kThreads, 0, st>>>(q16, k16, v16, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_split_kv_partial(const void* q, const void* kc, const void* vc,
+                                   const int32_t* page_table, int pt_stride,
+                                   const int32_t* ctx_lens, int B, int Hq, int Hkv,
+                                   int64_t num_phys_pages, int num_splits, float sm_scale,
+                                   int kv_dtype, float* o_part, float* lse_part,
+                                   hipStream_t st) {
+  const int G = Hq / Hkv;
+  const dim3 grid(static_cast<unsigned>(num_splits), static_cast<unsigned>(Hkv),
+                  static_cast<unsigned>(B));
+  const float scale = static_cast<float>(static_cast<double>(sm_scale) * 1.4426950408889634);
+  if (kv_dtype == MI_F16)
+    return launch_group<MI_F16>(G, grid, st, q, kc, vc, page_table, pt_stride, ctx_lens, Hkv,
+                                num_phys_pages, num_splits, scale, o_part, lse_part);
+  return launch_group<MI_BF16>(G, grid, st, q, kc, vc, page_table, pt_stride, ctx_lens, Hkv,
+                               num_phys_pages, num_splits, scale, o_part, lse_part);
+}
+
+}  // namespace mi

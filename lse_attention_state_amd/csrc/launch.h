@@ -1,0 +1,23 @@
+// Internal launchers behind the C ABI. Arguments are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mi {
+
+hipError_t launch_merge_state(const void* va, const float* sa, const void* vb, const float* sb,
+                              void* vo, float* so, int64_t rows, int D, int dt_in, int dt_out,
+                              hipStream_t stream);
+
+hipError_t launch_merge_states(const void* v, const float* s, void* vo, float* so, int64_t S,
+                               int N, int H, int D, int dt_in, int dt_out, hipStream_t stream);
+
+hipError_t launch_split_kv_partial(const void* q, const void* kc, const void* vc,
+                                   const int32_t* page_table, int pt_stride,
+                                   const int32_t* ctx_lens, int B, int Hq, int Hkv,
+                                   int64_t num_phys_pages, int num_splits, float sm_scale,
+                                   int kv_dtype, float* o_part, float* lse_part,
+                                   hipStream_t stream);
+
+}  // namespace mi
