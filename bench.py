@@ -1,0 +1,344 @@
+"""Benchmark: one step = one pass of the attention-state hot path on one GPU.
+
+A step runs, on synthetic data resident in HBM:
+  1. merge_state   bf16 S=32768, H=32, D=128 (1% of rows with both states empty)
+  2. merge_states  fp16 S=65536, N=4, H=8, D=128, 10% empty states (the N-state
+                   layout of the S=64 parity case at a size that streams HBM)
+  3. split-KV decode fp16 B=1, ctx=32768, Hq=32, Hkv=8, D=128, PAGE=16: the
+                   planner picks the split count (64), then pass 1 and the
+                   combine (the two launches mi_split_kv_decode makes)
+Inputs are rotated across copies so that consecutive uses of one buffer are
+separated by far more traffic than the 256 MB Infinity Cache holds.
+
+Output: one JSON line. value = algorithmic HBM bytes of a step / step time
+(GB/s, 1e9). Per-kernel durations come from HIP events recorded on the stream
+the kernels run on; the roofline object describes the kernel that takes the
+most time in a step. cpu_baseline times the fp64 CPU oracle on a bounded
+sample of the same inputs.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "HBM GB/s (% of peak) for merge_states + split-KV decode µs at B=1 ctx=32K"
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def to_dev(bits, dt, torch):
+    if dt == "f32":
+        return torch.from_numpy(np.ascontiguousarray(bits, np.float32)).cuda()
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[dt]
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tdt).cuda()
+
+
+class Raw:
+    """A C-ABI entry point bound to precomputed arguments: one ctypes call per
+    launch, so the host enqueues far faster than the GPU drains."""
+
+    def __init__(self, mi, name, *args):
+        import ctypes
+        self.fn = getattr(mi.lib(), name)
+        conv = []
+        for a in args:
+            if hasattr(a, "data_ptr"):
+                conv.append(ctypes.c_void_p(a.data_ptr()))
+            elif isinstance(a, float):
+                conv.append(ctypes.c_float(a))
+            else:
+                conv.append(a)
+        self.args = conv
+        self.name = name
+
+    def __call__(self):
+        rc = self.fn(*self.args)
+        if rc != 0:
+            raise RuntimeError(f"{self.name} returned {rc}")
+
+
+class Timer:
+    """Pairs of HIP events on the current stream, averaged per label."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def start(self, label):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.setdefault(label, []).append([e, None])
+
+    def stop(self, label):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs[label][-1][1] = e
+
+    def mean_us(self, label):
+        ps = self.pairs[label]
+        return 1000.0 * sum(a.elapsed_time(b) for a, b in ps) / len(ps)
+
+    def reset(self):
+        self.pairs = {}
+
+
+def build_workload(torch, mi, inputs):
+    """Device buffers, algorithmic bytes and launch closures for one step."""
+    parts = []
+
+    # 1. merge_state, bf16 [32768, 32, 128]
+    ms = inputs.merge_state_case(1002, S=32768, H=32, D=128, dtype="bf16")
+    rows = 32768 * 32
+    ms_copies = []
+    for c in range(2):
+        va = to_dev(ms["va"], "bf16", torch) if c == 0 else ms_copies[0][0].roll(1, 0)
+        vb = to_dev(ms["vb"], "bf16", torch) if c == 0 else ms_copies[0][2].roll(1, 0)
+        sa = torch.from_numpy(ms["sa"]).cuda() if c == 0 else ms_copies[0][1].roll(1, 0)
+        sb = torch.from_numpy(ms["sb"]).cuda() if c == 0 else ms_copies[0][3].roll(1, 0)
+        ms_copies.append((va, sa, vb, sb))
+    ms_out = torch.empty_like(ms_copies[0][0])
+    ms_sout = torch.empty_like(ms_copies[0][1])
+    ms_bytes = rows * (3 * 128 * 2 + 3 * 4)
+
+    stream = torch.cuda.current_stream().cuda_stream
+    import ctypes
+    st = ctypes.c_void_p(stream)
+    ms_calls = [Raw(mi, "mi_merge_state", va, sa, vb, sb, ms_out, ms_sout, rows, 1, 128,
+                    mi.MI_BF16, mi.MI_BF16, st) for (va, sa, vb, sb) in ms_copies]
+
+    def run_ms(i):
+        ms_calls[i % 2]()
+
+    parts.append(dict(name="merge_state", kernel="merge_state_kernel", bytes=ms_bytes, run=run_ms,
+                      shape="bf16 S=32768 H=32 D=128"))
+
+    # 2. merge_states, fp16 [65536, 4, 8, 128]
+    mss = inputs.merge_states_case(1001, S=65536, N=4, H=8, D=128, dtype="f16")
+    mss_v = to_dev(mss["v"], "f16", torch)
+    mss_s = torch.from_numpy(mss["s"]).cuda()
+    mss_vo = torch.empty((65536, 8, 128), dtype=torch.float16, device="cuda")
+    mss_so = torch.empty((65536, 8), dtype=torch.float32, device="cuda")
+    mss_bytes = 65536 * 8 * (4 * 128 * 2 + 4 * 4 + 128 * 2 + 4)
+
+    mss_call = Raw(mi, "mi_merge_states", mss_v, mss_s, mss_vo, mss_so, 65536, 4, 8, 128,
+                   mi.MI_F16, mi.MI_F16, st)
+
+    def run_mss(i):
+        mss_call()
+
+    parts.append(dict(name="merge_states", kernel="merge_states_kernel", bytes=mss_bytes,
+                      run=run_mss, shape="f16 S=65536 N=4 H=8 D=128"))
+
+    # 3. split-KV decode, fp16 B=1 ctx=32768 Hq=32 Hkv=8 D=128 PAGE=16
+    ctx_host = np.array([32768], np.int32)
+    dec = inputs.paged_kv_case(1003, ctx_host, 32, 8, 128, 16, dtype="f16")
+    q = to_dev(dec["q"], "f16", torch)
+    kv_copies = []
+    k0, v0 = to_dev(dec["k"], "f16", torch), to_dev(dec["v"], "f16", torch)
+    for c in range(4):
+        kv_copies.append((k0, v0) if c == 0 else (k0.clone(), v0.clone()))
+    pt = torch.from_numpy(dec["page_table"]).cuda()
+    ctx = torch.from_numpy(dec["ctx_lens"]).cuda()
+    splits = mi.plan_splits(ctx_host, 8, 16)
+    o_part = torch.empty((1, 32, splits, 128), dtype=torch.float32, device="cuda")
+    lse_part = torch.empty((1, 32, splits), dtype=torch.float32, device="cuda")
+    o = torch.empty((1, 32, 128), dtype=torch.float16, device="cuda")
+    lse = torch.empty((1, 32), dtype=torch.float32, device="cuda")
+    kv_bytes = 2 * 32768 * 8 * 128 * 2
+    part_bytes = 32 * splits * (128 + 1) * 4
+    dec_partial_bytes = kv_bytes + q.numel() * 2 + pt.numel() * 4 + 4 + part_bytes
+    dec_combine_bytes = part_bytes + 32 * (128 * 2 + 4)
+
+    def plan(i):
+        assert mi.plan_splits(ctx_host, 8, 16) == splits
+
+    scale = float(dec["sm_scale"])
+    partial_calls = [Raw(mi, "mi_split_kv_partial", q, k, v, pt, 2048, ctx, 1, 32, 8, 128, 16,
+                         2048, splits, scale, mi.MI_F16, o_part, lse_part, st)
+                     for (k, v) in kv_copies]
+    combine_call = Raw(mi, "mi_merge_states", o_part, lse_part, o, lse, 32, splits, 1, 128,
+                       mi.MI_F32, mi.MI_F16, st)
+    decode_calls = [Raw(mi, "mi_split_kv_decode", q, k, v, pt, 2048, ctx, 1, 32, 8, 128, 16, 2048,
+                        splits, scale, mi.MI_F16, o_part, lse_part, o, lse, mi.MI_F16, st)
+                    for (k, v) in kv_copies]
+    counters = torch.zeros((1, 8), dtype=torch.int32, device="cuda")
+    fused_calls = [Raw(mi, "mi_split_kv_decode_fused", q, k, v, pt, 2048, ctx, 1, 32, 8, 128, 16,
+                       2048, splits, scale, mi.MI_F16, o_part, lse_part, counters, o, lse,
+                       mi.MI_F16, st)
+                   for (k, v) in kv_copies]
+
+    def run_decode(i):
+        fused_calls[i % 4]()
+
+    parts.append(dict(name="split_kv_decode", kernel="split_kv_partial_kernel",
+                      bytes=dec_partial_bytes + dec_combine_bytes, run=run_decode, host=plan,
+                      shape=(f"f16 B=1 ctx=32768 Hq=32 Hkv=8 D=128 PAGE=16 splits={splits}, "
+                             "pass 1 and combine in one launch")))
+    host = dict(ms=ms, mss=mss, dec=dec, splits=splits, decode_calls=decode_calls,
+                fused_calls=fused_calls, partial_calls=partial_calls, combine_call=combine_call,
+                plan=plan)
+    return parts, host
+
+
+def cpu_baseline(host, oracle):
+    """Time the oracle on a bounded sample of the step's inputs."""
+    threads = len(os.sched_getaffinity(0))
+    ms, mss, dec = host["ms"], host["mss"], host["dec"]
+    n_ms = 32768 * 32 // 2            # half of the merge_state rows
+    n_mss = 65536 // 2                # half of the merge_states positions
+    t0 = time.perf_counter()
+    oracle.merge_state(ms["va"].reshape(-1, 128)[:n_ms], ms["sa"].reshape(-1)[:n_ms],
+                       ms["vb"].reshape(-1, 128)[:n_ms], ms["sb"].reshape(-1)[:n_ms], "bf16",
+                       threads)
+    oracle.merge_states(mss["v"][:n_mss], mss["s"][:n_mss], "f16", threads)
+    oracle.attention(dec["q"], dec["k"], dec["v"], dec["page_table"], dec["ctx_lens"],
+                     dec["sm_scale"], "f16", "f16", threads)
+    dt = time.perf_counter() - t0
+    sample_bytes = (n_ms * (3 * 128 * 2 + 3 * 4) + n_mss * 8 * (4 * 128 * 2 + 4 * 4 + 128 * 2 + 4)
+                    + 2 * 32768 * 8 * 128 * 2)
+    return {"value": round(sample_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": ("fp64 oracle: merge_state on half of the rows, merge_states on half of "
+                       "the positions, unsplit decode attention for all 32 heads at ctx=32768; "
+                       f"{dt:.2f} s wall; GB/s counts the same algorithmic bytes as the GPU")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import lse_attention_state_amd as mi
+    from lse_attention_state_amd import inputs
+
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 5}))
+        return
+
+    parts, host = build_workload(torch, mi, inputs)
+    timer = Timer(torch)
+
+    def step(i, timed):
+        for p in parts:
+            if "host" in p:
+                p["host"](i)        # host-side planning, outside the event brackets
+            if timed:
+                timer.start(p["name"])
+            p["run"](i)
+            if timed:
+                timer.stop(p["name"])
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    # Timed region 1: the steps alone (no events between kernels).
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        step(i, False)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1000.0 * wall / args.steps
+    gpu_ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    # Timed region 2: the same steps with an event pair around every kernel.
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+
+    # Decode end to end, back to back with rotated K/V copies: single launch,
+    # and the two-launch form (pass 1, then the combine).
+    for label, calls in (("decode", host["fused_calls"]), ("decode_two_launch", host["decode_calls"])):
+        for i in range(args.steps):
+            host["plan"](i)
+            timer.start(label)
+            calls[i % 4]()
+            timer.stop(label)
+        torch.cuda.synchronize()
+    for i in range(args.steps):
+        timer.start("split_kv_partial")
+        host["partial_calls"][i % 4]()
+        timer.stop("split_kv_partial")
+        timer.start("combine")
+        host["combine_call"]()
+        timer.stop("combine")
+    torch.cuda.synchronize()
+
+    step_bytes = sum(p["bytes"] for p in parts)
+    value = step_bytes / (ms_per_step / 1000.0) / 1e9
+    per = []
+    for p in parts:
+        us = timer.mean_us(p["name"])
+        gbs = p["bytes"] / (us * 1e-6) / 1e9
+        per.append({"kernel": p["name"], "shape": p["shape"], "us": round(us, 2),
+                    "bytes": p["bytes"], "GB/s": round(gbs, 1),
+                    "frac": round(gbs / HBM_PEAK_GBS, 4)})
+    dom = max(per, key=lambda r: r["us"])
+    traffic = None
+    if os.path.exists(COUNTERS_FILE):
+        with open(COUNTERS_FILE) as f:
+            tr = json.load(f).get(dom["kernel"])
+        if tr is not None:
+            traffic = tr.get("bytes_per_launch")
+    roofline = {"bound": "hbm", "achieved": dom["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": dom["frac"], "traffic": traffic, "kernel": dom["kernel"]}
+    decode_us = timer.mean_us("decode")
+    dec_bytes = [p for p in parts if p["name"] == "split_kv_decode"][0]["bytes"]
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": ("merge_state bf16 S=32768 H=32 D=128 + merge_states f16 "
+                                "S=65536 N=4 H=8 D=128 + split-KV decode f16 B=1 ctx=32768 "
+                                f"Hq=32 Hkv=8 D=128 PAGE=16 splits={host['splits']}"),
+                   "step_bytes": step_bytes},
+        "frac_of_peak": round(value / HBM_PEAK_GBS, 4),
+        "gpu_ms_per_step": round(gpu_ms_per_step, 4),
+        "decode_us": round(decode_us, 2),
+        "decode_GBs": round(dec_bytes / (decode_us * 1e-6) / 1e9, 1),
+        "decode_two_launch_us": round(timer.mean_us("decode_two_launch"), 2),
+        "decode_pass1_us": round(timer.mean_us("split_kv_partial"), 2),
+        "decode_combine_us": round(timer.mean_us("combine"), 2),
+        "kernels": per,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        line["cpu_baseline"] = cpu_baseline(host, oracle)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

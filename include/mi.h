@@ -152,6 +152,27 @@ mi_status mi_split_kv_decode(const void* q, const void* k_cache, const void* v_c
                              mi_dtype kv_dtype, float* o_part, float* lse_part, void* o,
                              float* lse, mi_dtype out_dtype, void* stream);
 
+/*
+ * Split-KV paged decode in a single launch ("L3 hints: split-KV decode and LSE
+ * merge", sections 1 and 3): pass 1 exactly as mi_split_kv_partial, after which
+ * the last workgroup to finish for each (sequence, kv head) merges the splits
+ * of that kv head's query heads and writes o and lse. Same results as
+ * mi_split_kv_decode up to the order of rounding; saves the second launch.
+ *   counters : [B, Hkv] int32 device workspace used to find the last
+ *              workgroup. It must be all zero before the first call; every call
+ *              leaves it all zero again. Calls that share one counters buffer
+ *              must not run concurrently (different streams race).
+ * All other arguments, layouts and rules as mi_split_kv_decode; o_part and
+ * lse_part are left holding the partials.
+ */
+mi_status mi_split_kv_decode_fused(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* page_table, int32_t pt_stride,
+                                   const int32_t* ctx_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                                   int32_t D, int32_t page_size, int64_t num_phys_pages,
+                                   int32_t num_splits, float sm_scale, mi_dtype kv_dtype,
+                                   float* o_part, float* lse_part, int32_t* counters, void* o,
+                                   float* lse, mi_dtype out_dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

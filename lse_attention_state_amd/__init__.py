@@ -38,6 +38,8 @@ SIGNATURES = {
                             _F, ctypes.c_int, _P, _P, _P],
     "mi_split_kv_decode": [_P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I64, _I32, _F,
                            ctypes.c_int, _P, _P, _P, _P, ctypes.c_int, _P],
+    "mi_split_kv_decode_fused": [_P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I64,
+                                 _I32, _F, ctypes.c_int, _P, _P, _P, _P, _P, ctypes.c_int, _P],
 }
 
 
@@ -211,6 +213,39 @@ def split_kv_decode(q, k_cache, v_cache, page_table, ctx_lens, num_splits: int, 
           page_table.shape[1], _ptr(ctx_lens), B, Hq, Hkv, D, page, P, num_splits,
           float(sm_scale), _dt(q), _ptr(o_part), _ptr(lse_part), _ptr(out), _ptr(lse),
           _dt(out), _stream(q))
+    if return_partials:
+        return out, lse, o_part, lse_part
+    return out, lse
+
+
+def split_kv_decode_fused(q, k_cache, v_cache, page_table, ctx_lens, num_splits: int,
+                          sm_scale: float, counters=None, out_dtype=None, o_part=None,
+                          lse_part=None, out=None, lse=None, return_lse=True,
+                          return_partials=False):
+    """Single-launch decode -> (o [B, Hq, D], lse [B, Hq][, o_part, lse_part]).
+
+    ``counters`` is an int32 [B, Hkv] device workspace that must be zero before
+    the first call; each call leaves it zero. It is allocated (zeroed) when not
+    given."""
+    B, Hq, Hkv, D, page, P = _decode_args(q, k_cache, v_cache, page_table, ctx_lens)
+    out_dtype = out_dtype or (out.dtype if out is not None else q.dtype)
+    if counters is None:
+        counters = torch.zeros((B, Hkv), dtype=torch.int32, device=q.device)
+    if counters.dtype != torch.int32 or counters.numel() < B * Hkv:
+        raise ValueError("counters must be int32 with at least B * Hkv entries")
+    if o_part is None:
+        o_part = torch.empty((B, Hq, num_splits, D), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((B, Hq, num_splits), dtype=torch.float32, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check_cuda(o_part, lse_part, out, lse, counters)
+    _call("mi_split_kv_decode_fused", _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+          page_table.shape[1], _ptr(ctx_lens), B, Hq, Hkv, D, page, P, num_splits,
+          float(sm_scale), _dt(q), _ptr(o_part), _ptr(lse_part), _ptr(counters), _ptr(out),
+          _ptr(lse), _dt(out), _stream(q))
     if return_partials:
         return out, lse, o_part, lse_part
     return out, lse

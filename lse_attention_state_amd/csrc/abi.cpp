@@ -225,6 +225,37 @@ mi_status mi_split_kv_partial(const void* q, const void* k_cache, const void* v_
                                               static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+
+// Shared by the two-launch and the fused decode: validation of the outputs
+// (and of the counters workspace when it is used).
+mi_status check_decode_outputs(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* page_table, const int32_t* ctx_lens,
+                               const float* o_part, const float* lse_part,
+                               const int32_t* counters, bool need_counters, const void* o,
+                               const float* lse, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                               mi_dtype out_dtype, const DecodeShape& shp) {
+  if (!o || (need_counters && !counters)) return MI_ERR_NULL;
+  if (!dtype_ok(out_dtype)) return MI_ERR_DTYPE;
+  if (!aligned(o, 16) || !aligned(lse, 4) || !aligned(counters, 4)) return MI_ERR_UNSUPPORTED;
+  const int64_t o_bytes = int64_t(B) * Hq * D * dtype_bytes(out_dtype);
+  const int64_t lse_bytes = int64_t(B) * Hq * 4;
+  const int64_t cnt_bytes = need_counters ? int64_t(B) * Hkv * 4 : 0;
+  const void* all[7] = {q, k_cache, v_cache, page_table, ctx_lens, o_part, lse_part};
+  const int64_t all_b[7] = {shp.q_bytes, shp.cache_bytes, shp.cache_bytes, shp.pt_bytes,
+                            shp.ctx_bytes, shp.opart_bytes, shp.lpart_bytes};
+  for (int i = 0; i < 7; ++i)
+    if (overlaps(o, o_bytes, all[i], all_b[i]) || overlaps(lse, lse_bytes, all[i], all_b[i]) ||
+        overlaps(counters, cnt_bytes, all[i], all_b[i]))
+      return MI_ERR_ALIAS;
+  if (overlaps(o, o_bytes, lse, lse_bytes) || overlaps(counters, cnt_bytes, o, o_bytes) ||
+      overlaps(counters, cnt_bytes, lse, lse_bytes))
+    return MI_ERR_ALIAS;
+  return MI_OK;
+}
+
+}  // namespace
+
 mi_status mi_split_kv_decode(const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* page_table, int32_t pt_stride, const int32_t* ctx_lens,
                              int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size,
@@ -237,17 +268,9 @@ mi_status mi_split_kv_decode(const void* q, const void* k_cache, const void* v_c
                               page_size, num_phys_pages, num_splits, kv_dtype, o_part, lse_part,
                               &shp);
   if (st != MI_OK) return st;
-  if (!dtype_ok(out_dtype)) return MI_ERR_DTYPE;
-  if (!aligned(o, 16) || !aligned(lse, 4)) return MI_ERR_UNSUPPORTED;
-  const int64_t o_bytes = int64_t(B) * Hq * D * dtype_bytes(out_dtype);
-  const int64_t lse_bytes = int64_t(B) * Hq * 4;
-  const void* all[7] = {q, k_cache, v_cache, page_table, ctx_lens, o_part, lse_part};
-  const int64_t all_b[7] = {shp.q_bytes, shp.cache_bytes, shp.cache_bytes, shp.pt_bytes,
-                            shp.ctx_bytes, shp.opart_bytes, shp.lpart_bytes};
-  for (int i = 0; i < 7; ++i)
-    if (overlaps(o, o_bytes, all[i], all_b[i]) || overlaps(lse, lse_bytes, all[i], all_b[i]))
-      return MI_ERR_ALIAS;
-  if (overlaps(o, o_bytes, lse, lse_bytes)) return MI_ERR_ALIAS;
+  st = check_decode_outputs(q, k_cache, v_cache, page_table, ctx_lens, o_part, lse_part, nullptr,
+                            false, o, lse, B, Hq, Hkv, D, out_dtype, shp);
+  if (st != MI_OK) return st;
   if (B == 0) return MI_OK;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = mi::launch_split_kv_partial(q, k_cache, v_cache, page_table, pt_stride, ctx_lens,
@@ -257,6 +280,30 @@ mi_status mi_split_kv_decode(const void* q, const void* k_cache, const void* v_c
   // The combine: o_part [B, Hq, splits, D] is merge_states' [S = B*Hq, N = splits, H = 1, D].
   return from_hip(mi::launch_merge_states(o_part, lse_part, o, lse, int64_t(B) * Hq, num_splits,
                                           1, D, MI_F32, out_dtype, s));
+}
+
+mi_status mi_split_kv_decode_fused(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* page_table, int32_t pt_stride,
+                                   const int32_t* ctx_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                                   int32_t D, int32_t page_size, int64_t num_phys_pages,
+                                   int32_t num_splits, float sm_scale, mi_dtype kv_dtype,
+                                   float* o_part, float* lse_part, int32_t* counters, void* o,
+                                   float* lse, mi_dtype out_dtype, void* stream) {
+  if (!o || !counters) return MI_ERR_NULL;
+  DecodeShape shp;
+  mi_status st = check_decode(q, k_cache, v_cache, page_table, pt_stride, ctx_lens, B, Hq, Hkv, D,
+                              page_size, num_phys_pages, num_splits, kv_dtype, o_part, lse_part,
+                              &shp);
+  if (st != MI_OK) return st;
+  st = check_decode_outputs(q, k_cache, v_cache, page_table, ctx_lens, o_part, lse_part, counters,
+                            true, o, lse, B, Hq, Hkv, D, out_dtype, shp);
+  if (st != MI_OK) return st;
+  if (B == 0) return MI_OK;
+  return from_hip(mi::launch_split_kv_partial(q, k_cache, v_cache, page_table, pt_stride,
+                                              ctx_lens, B, Hq, Hkv, num_phys_pages, num_splits,
+                                              sm_scale, kv_dtype, o_part, lse_part,
+                                              static_cast<hipStream_t>(stream), counters, o, lse,
+                                              out_dtype));
 }
 
 }  // extern "C"

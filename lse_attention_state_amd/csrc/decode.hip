@@ -38,13 +38,22 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kPage = 16;
-constexpr int kWaves = 4;
+// Pages in flight per wave, and page groups per workgroup (4 waves each).
+#ifndef MI_DECODE_DEPTH
+#define MI_DECODE_DEPTH 8
+#endif
+#ifndef MI_DECODE_PAGE_GROUPS
+#define MI_DECODE_PAGE_GROUPS 1
+#endif
+constexpr int kDepth = MI_DECODE_DEPTH;
+constexpr int kPageGroups = MI_DECODE_PAGE_GROUPS;
+constexpr int kWaves = 4 * kPageGroups;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kDepth = 8;
-static_assert(64 % kDepth == 0, "page-id chunks hold whole prefetch batches");
 constexpr float kRescaleSlack = 8.0f;
 // Word 3 of a gfx9 buffer descriptor for raw (untyped, unswizzled) access.
 constexpr int kBufferFlags = 0x00020000;
+// s_waitcnt immediate (gfx9 encoding) for vmcnt(0), other counters unconstrained.
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 template <int DT>
 __device__ __forceinline__ float dot8(const u32x4_t& q, const u32x4_t& k) {
@@ -73,21 +82,94 @@ __device__ __forceinline__ void unpack8(const u32x4_t& w, float (&x)[8]) {
   }
 }
 
-template <int DT, int G>
+// The combine of one (sequence, query head) row by one wave: merge the
+// num_splits partial states o_part[row, :, :], lse_part[row, :] ("L3 hints:
+// split-KV decode and LSE merge", section 3) into o[row, :] (dtype DTO) and
+// lse[row] (base 2, optional). Lane l owns the 8-element chunk (l%16)*8 of D
+// for the splits k = l/16 (mod 4); each pass keeps 8 of its splits' loads in
+// flight, then the four split sub-groups are merged across lanes.
+template <int DTO>
+__device__ void combine_row(const float* o_part, const float* lse_part, int64_t row,
+                            int num_splits, void* o, float* lse, int lane) {
+  const int c = lane & 15;
+  const int sg = lane >> 4;
+  const float* lp = lse_part + row * num_splits;
+  const float* op = o_part + row * num_splits * kD + c * 8;
+  float m = -kInf, z = 0.0f, acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+  for (int k0 = sg; k0 < num_splits; k0 += 32) {
+    float sv[8], x[8][8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = k0 + 4 * u;
+      const int kk = k < num_splits ? k : 0;
+      sv[u] = lp[kk];
+      load8<MI_F32>(op, static_cast<int64_t>(kk) * kD, x[u]);
+    }
+    float cm = m;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      sv[u] = k0 + 4 * u < num_splits ? sanitize_lse(sv[u]) : -kInf;
+      cm = __builtin_fmaxf(cm, sv[u]);
+    }
+    const float keep = guarded_exp2(m - cm);
+    z *= keep;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= keep;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float w = guarded_exp2(sv[u] - cm);
+      z += w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = (w > 0.0f) ? __builtin_fmaf(w, x[u][e], acc[e]) : acc[e];
+    }
+    m = cm;
+  }
+#pragma unroll
+  for (int sh = 16; sh <= 32; sh <<= 1) {
+    const float mo = shfl_xor(m, sh);
+    const float zo = shfl_xor(z, sh);
+    const float M = __builtin_fmaxf(m, mo);
+    const float ws = guarded_exp2(m - M);
+    const float wo = guarded_exp2(mo - M);
+    z = z * ws + zo * wo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = acc[e] * ws + shfl_xor(acc[e], sh) * wo;
+    m = M;
+  }
+  if (sg == 0) {
+    const float inv = guarded_inv(z);
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = acc[e] * inv;
+    store8<DTO>(o, row * kD + c * 8, y);
+    if (lse != nullptr && c == 0) lse[row] = (z > 0.0f) ? m + hw_log2(z) : -kInf;
+  }
+}
+
+// DTO < 0: pass 1 only. DTO = an output dtype: pass 1 fused with the combine
+// (the last workgroup of each (sequence, kv head) to finish merges the splits).
+template <int DT, int G, int DTO>
 __global__ __launch_bounds__(kThreads) void split_kv_partial_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ page_table, int pt_stride,
     const int32_t* __restrict__ ctx_lens, int Hkv, int64_t num_phys, int num_splits,
-    float qk_scale_log2, float* __restrict__ o_part, float* __restrict__ lse_part) {
+    float qk_scale_log2, float* __restrict__ o_part, float* __restrict__ lse_part,
+    int32_t* __restrict__ counters, void* __restrict__ o, float* __restrict__ lse) {
   __shared__ float lds_acc[kWaves][G][kD];
   __shared__ float lds_ml[kWaves][G][2];
 
   const int split = blockIdx.x;
   const int hkv = blockIdx.y;
   const int b = blockIdx.z;
-  const int wave = threadIdx.x >> 6;
+  // The wave index is uniform across the wave: readfirstlane tells the
+  // compiler so (it keeps wave-derived values in scalar registers).
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int slot = wave * 4 + (lane >> 4);
+  const int pg = wave >> 2;          // page group: pages pg, pg + kPageGroups, ...
+  const int quarter = wave & 3;      // token slots 4*quarter .. 4*quarter+3 of a page
+  const int slot = quarter * 4 + (lane >> 4);
   const int d0 = (lane & 15) * 8;
   const int Hq = Hkv * G;
 
@@ -114,8 +196,8 @@ __global__ __launch_bounds__(kThreads) void split_kv_partial_kernel(
     for (int j = 0; j < 8; ++j) acc[h][j] = 0.0f;
   }
 
-  // Page ids: lane l holds the id of page (chunk*64 + l) of the split; the
-  // issuing code broadcasts them with readlane, off the memory critical path.
+  // Page ids: lane l holds the id of page (c0 + l) of the split for the chunk
+  // starting at page c0; issues broadcast them with readlane.
   const int32_t* pt = page_table + static_cast<int64_t>(b) * pt_stride + p0;
   auto load_ids = [&](int first) {
     const int i = first + lane;
@@ -127,14 +209,17 @@ __global__ __launch_bounds__(kThreads) void split_kv_partial_kernel(
   // and page ids outside [0, num_phys), get a descriptor with no records: the
   // hardware returns zeros for them without touching memory, so every
   // prefetch below is unconditional.
-  const int lane_bytes = (wave * 64 + lane) * 16;
+  const int lane_bytes = (quarter * 64 + lane) * 16;
   const int64_t tile_elems = static_cast<int64_t>(kPage) * kD;
   u32x4_t kb[kDepth], vb[kDepth];
   bool ok[kDepth];
   int ids = 0;
-  auto issue = [&](int i, int j) {
-    const int32_t phys = __builtin_amdgcn_readlane(ids, i & 63);
-    ok[j] = i < npages && phys >= 0 && phys < num_phys;
+  // issue(k, n, j): the wave's k-th page of the current chunk (chunk-relative
+  // page r = pg + k*kPageGroups of n) into register slot j.
+  auto issue = [&](int k, int n, int j) {
+    const int r = pg + k * kPageGroups;
+    const int32_t phys = __builtin_amdgcn_readlane(ids, r & 63);
+    ok[j] = r < n && phys >= 0 && phys < num_phys;
     const int64_t tile = (static_cast<int64_t>(ok[j] ? phys : 0) * Hkv + hkv) * tile_elems;
     const int records = ok[j] ? static_cast<int>(tile_elems * 2) : 0;
     const __amdgpu_buffer_rsrc_t rk =
@@ -190,31 +275,40 @@ __global__ __launch_bounds__(kThreads) void split_kv_partial_kernel(
       for (int e = 0; e < 8; ++e) acc[h][e] = __builtin_fmaf(p, v[e], acc[h][e]);
     }
   };
-  // The only page that can hold slots at or past ctx is the sequence's last.
-  const bool tail_partial = (ctx % kPage) != 0;
-  const int last_page = ctx / kPage;  // logical index of a partial last page
+  // The only page that can hold slots at or past ctx is the sequence's last
+  // page when ctx is not a multiple of the page size. If this split holds it,
+  // it is taken out of the pipelined loop (which then needs no masking) and
+  // handled once at the end with the masked step.
+  const bool has_tail = npages > 0 && (ctx % kPage) != 0 && p1 - 1 == ctx / kPage;
+  const int nmain = npages - (has_tail ? 1 : 0);
 
-  if (npages > 0) {
-    const int iters = (npages + kDepth - 1) / kDepth * kDepth;
-    ids = load_ids(0);
+  // Pages are processed in chunks of 64 (one VGPR of page ids per chunk).
+  // Within a chunk the loop body holds only the K/V loads, each slot being
+  // re-issued right after it is consumed; the scheduling barrier keeps that
+  // order so every consume waits only for the load issued kDepth pages earlier.
+  for (int c0 = 0; c0 < nmain; c0 += 64) {
+    const int n = nmain - c0 < 64 ? nmain - c0 : 64;
+    const int n_local = n > pg ? (n - pg + kPageGroups - 1) / kPageGroups : 0;
+    ids = load_ids(c0);
 #pragma unroll
-    for (int j = 0; j < kDepth; ++j) issue(j, j);
+    for (int j = 0; j < kDepth; ++j) {
+      issue(j, n, j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const int iters = (n_local + kDepth - 1) / kDepth * kDepth;
     for (int base = 0; base < iters; base += kDepth) {
-      // Pages base+kDepth .. base+2*kDepth-1 are issued in this batch; they
-      // share one 64-page chunk of ids because kDepth divides 64.
-      if (((base + kDepth) & 63) == 0) ids = load_ids(base + kDepth);
 #pragma unroll
       for (int j = 0; j < kDepth; ++j) {
-        const int i = base + j;
-        // Every slot is consumed on every path (a skipped consume would make
-        // the compiler drain all loads before the slot's registers are reused).
-        if (tail_partial && p0 + i == last_page)
-          consume(i, j, std::true_type{});
-        else
-          consume(i, j, std::false_type{});
-        issue(i + kDepth, j);
+        consume(c0 + pg + (base + j) * kPageGroups, j, std::false_type{});
+        issue(base + j + kDepth, n, j);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+  }
+  if (has_tail && nmain % kPageGroups == pg) {
+    ids = load_ids(nmain & ~63);
+    issue((nmain & 63) / kPageGroups, (nmain & 63) + 1, 0);
+    consume(nmain, 0, std::true_type{});
   }
 
   // Merge the four token rows of the wave (lanes l, l^16, l^32, l^48).
@@ -265,34 +359,86 @@ __global__ __launch_bounds__(kThreads) void split_kv_partial_kernel(
     const float inv = guarded_inv(Z);
     const int64_t row = static_cast<int64_t>(b) * Hq + hkv * G + h;
     float* out = o_part + (row * num_splits + split) * kD + 2 * lane;
-    *reinterpret_cast<float2*>(out) = make_float2(o0 * inv, o1 * inv);
-    if (lane == 0) lse_part[row * num_splits + split] = (Z > 0.0f) ? M + hw_log2(Z) : -kInf;
+    const float2 res = make_float2(o0 * inv, o1 * inv);
+    const float lse_val = (Z > 0.0f) ? M + hw_log2(Z) : -kInf;
+    if constexpr (DTO >= 0) {
+      // Agent-scope stores are written through to the device coherence point,
+      // so another XCD can read them without a writeback of this XCD's L2.
+      __hip_atomic_store(reinterpret_cast<uint64_t*>(out), __builtin_bit_cast(uint64_t, res),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0)
+        __hip_atomic_store(lse_part + row * num_splits + split, lse_val, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      *reinterpret_cast<float2*>(out) = res;
+      if (lane == 0) lse_part[row * num_splits + split] = lse_val;
+    }
+  }
+
+  if constexpr (DTO >= 0) {
+    // Hand-off: every workgroup publishes its partials (agent-scope release)
+    // and bumps the (sequence, kv head) counter; the one that brings it to
+    // num_splits performs the acquire and merges all splits of its heads.
+    __shared__ int is_last;
+    // Publish: the partials above were written with write-through agent-scope
+    // stores; waiting for them to complete (vmcnt(0)) before the barrier and
+    // the counter update orders them before it without a whole-L2 writeback.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int prev = __hip_atomic_fetch_add(counters + static_cast<int64_t>(b) * Hkv + hkv, 1,
+                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      is_last = prev == num_splits - 1;
+    }
+    __syncthreads();
+    if (!is_last) return;
+    // Acquire at agent scope: drop stale lines before reading other
+    // workgroups' partials.
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    for (int h = wave; h < G; h += kWaves)
+      combine_row<DTO>(o_part, lse_part, static_cast<int64_t>(b) * Hq + hkv * G + h, num_splits,
+                       o, lse, lane);
+    if (threadIdx.x == 0) counters[static_cast<int64_t>(b) * Hkv + hkv] = 0;
   }
 }
 
-template <int DT>
+template <int DT, int DTO>
 hipError_t launch_group(int G, dim3 grid, hipStream_t st, const void* q, const void* kc,
                         const void* vc, const int32_t* pt, int pt_stride, const int32_t* ctx,
                         int Hkv, int64_t num_phys, int num_splits, float scale, float* o_part,
-                        float* lse_part) {
+                        float* lse_part, int32_t* counters, void* o, float* lse) {
   const uint16_t* q16 = static_cast<const uint16_t*>(q);
   const uint16_t* k16 = static_cast<const uint16_t*>(kc);
   const uint16_t* v16 = static_cast<const uint16_t*>(vc);
+#define MI_LAUNCH_G(GG)                                                                        \
+  split_kv_partial_kernel<DT, GG, DTO><<<grid, kThreads, 0, st>>>(                             \
+      q16, k16, v16, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part, \
+      counters, o, lse)
   switch (G) {
-    case 1:
-      split_kv_partial_kernel<DT, 1><<<grid, kThreads, 0, st>>>(q16, k16, v16, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part);
-      break;
-    case 2:
-      split_kv_partial_kernel<DT, 2><<<grid, kThreads, 0, st>>>(q16, k16, v16, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part);
-      break;
-    case 4:
-      split_kv_partial_kernel<DT, 4><<<grid, kThreads, 0, st>>>(q16, k16, v16, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part);
-      break;
-    default:
-      split_kv_partial_kernel<DT, 8><<<grid, kThreads, 0, st>>>(q16, k16, v16, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part);
-      break;
+    case 1: MI_LAUNCH_G(1); break;
+    case 2: MI_LAUNCH_G(2); break;
+    case 4: MI_LAUNCH_G(4); break;
+    default: MI_LAUNCH_G(8); break;
   }
+#undef MI_LAUNCH_G
   return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_dtype(int out_dtype, int G, dim3 grid, hipStream_t st, const void* q,
+                        const void* kc, const void* vc, const int32_t* pt, int pt_stride,
+                        const int32_t* ctx, int Hkv, int64_t num_phys, int num_splits, float scale,
+                        float* o_part, float* lse_part, int32_t* counters, void* o, float* lse) {
+  switch (out_dtype) {
+    case MI_F16:
+      return launch_group<DT, MI_F16>(G, grid, st, q, kc, vc, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part, counters, o, lse);
+    case MI_BF16:
+      return launch_group<DT, MI_BF16>(G, grid, st, q, kc, vc, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part, counters, o, lse);
+    case MI_F32:
+      return launch_group<DT, MI_F32>(G, grid, st, q, kc, vc, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part, counters, o, lse);
+    default:
+      return launch_group<DT, -1>(G, grid, st, q, kc, vc, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part, nullptr, nullptr, nullptr);
+  }
 }
 
 }  // namespace
@@ -302,16 +448,20 @@ hipError_t launch_split_kv_partial(const void* q, const void* kc, const void* vc
                                    const int32_t* ctx_lens, int B, int Hq, int Hkv,
                                    int64_t num_phys_pages, int num_splits, float sm_scale,
                                    int kv_dtype, float* o_part, float* lse_part,
-                                   hipStream_t st) {
+                                   hipStream_t st, int32_t* counters, void* o, float* lse,
+                                   int out_dtype) {
   const int G = Hq / Hkv;
   const dim3 grid(static_cast<unsigned>(num_splits), static_cast<unsigned>(Hkv),
                   static_cast<unsigned>(B));
   const float scale = static_cast<float>(static_cast<double>(sm_scale) * 1.4426950408889634);
+  const int dto = counters != nullptr ? out_dtype : -1;
   if (kv_dtype == MI_F16)
-    return launch_group<MI_F16>(G, grid, st, q, kc, vc, page_table, pt_stride, ctx_lens, Hkv,
-                                num_phys_pages, num_splits, scale, o_part, lse_part);
-  return launch_group<MI_BF16>(G, grid, st, q, kc, vc, page_table, pt_stride, ctx_lens, Hkv,
-                               num_phys_pages, num_splits, scale, o_part, lse_part);
+    return launch_dtype<MI_F16>(dto, G, grid, st, q, kc, vc, page_table, pt_stride, ctx_lens, Hkv,
+                                num_phys_pages, num_splits, scale, o_part, lse_part, counters, o,
+                                lse);
+  return launch_dtype<MI_BF16>(dto, G, grid, st, q, kc, vc, page_table, pt_stride, ctx_lens, Hkv,
+                               num_phys_pages, num_splits, scale, o_part, lse_part, counters, o,
+                               lse);
 }
 
 }  // namespace mi

@@ -18,6 +18,7 @@ hipError_t launch_split_kv_partial(const void* q, const void* kc, const void* vc
                                    const int32_t* ctx_lens, int B, int Hq, int Hkv,
                                    int64_t num_phys_pages, int num_splits, float sm_scale,
                                    int kv_dtype, float* o_part, float* lse_part,
-                                   hipStream_t stream);
+                                   hipStream_t stream, int32_t* counters = nullptr,
+                                   void* o = nullptr, float* lse = nullptr, int out_dtype = -1);
 
 }  // namespace mi

@@ -50,9 +50,10 @@ __global__ __launch_bounds__(kBlock) void merge_state_kernel(
     const float inv = guarded_inv(z);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      float t = (wa > 0.0f) ? wa * xa[j] : 0.0f;
-      t = (wb > 0.0f) ? __builtin_fmaf(wb, xb[j], t) : t;
-      y[j] = t * inv;
+      // Two rounded products and one add: the same bits for (a, b) and (b, a).
+      const float ta = (wa > 0.0f) ? wa * xa[j] : 0.0f;
+      const float tb = (wb > 0.0f) ? wb * xb[j] : 0.0f;
+      y[j] = (ta + tb) * inv;
     }
     store8<DTO>(vo, off, y);
   }
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(kBlock) void merge_state_kernel(
 // group g handles states n = g, g+G, ...; groups are merged through LDS.
 constexpr int kLdsFloats = 2048 + 512;  // rows_per_block * G * (8L + 2) <= 2048 + 512/L
 
-template <int DTI, int DTO>
+template <int DTI, int DTO, int kChunk>
 __global__ __launch_bounds__(kBlock) void merge_states_kernel(
     const void* __restrict__ v, const float* __restrict__ s, void* __restrict__ vo,
     float* __restrict__ so, int64_t rows, int N, int H, int D, int lanes_shift,
@@ -84,23 +85,50 @@ __global__ __launch_bounds__(kBlock) void merge_states_kernel(
   const int64_t pos = row_ok ? row / H : 0;
   const int h = row_ok ? static_cast<int>(row - pos * H) : 0;
 
+  // The group's states are taken kChunk at a time: all of a chunk's s and v
+  // loads are issued before any is used (so they are in flight together), then
+  // the chunk is folded into the running state (m, z, acc) with the merge rule.
   float m = -kInf;
   float z = 0.0f;
   float acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
   if (row_ok) {
-    for (int n = g; n < N; n += G) m = __builtin_fmaxf(m, sanitize_lse(s[(pos * N + n) * H + h]));
-    for (int n = g; n < N; n += G) {
-      const int64_t idx = (pos * N + n) * H + h;
-      const float w = guarded_exp2(sanitize_lse(s[idx]) - m);
-      z += w;
-      if (lane_ok) {
-        float x[8];
-        load8<DTI>(v, idx * D + d0, x);
+    for (int n0 = g; n0 < N; n0 += kChunk * G) {
+      float sv[kChunk];
+      float x[kChunk][8];
+      // Loads are unconditional (indices clamped to valid ones) and results
+      // are selected afterwards: a load under a lane mask followed by a
+      // zero-fill of the same registers would force a wait after every load.
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = (w > 0.0f) ? __builtin_fmaf(w, x[j], acc[j]) : acc[j];
+      for (int u = 0; u < kChunk; ++u) {
+        const int n = n0 + u * G;
+        const int64_t idx = (pos * N + (n < N ? n : 0)) * H + h;
+        sv[u] = s[idx];
+        load8<DTI>(v, idx * D + (lane_ok ? d0 : 0), x[u]);
       }
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) {
+        const bool in = n0 + u * G < N;
+        sv[u] = in ? sanitize_lse(sv[u]) : -kInf;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[u][j] = (in && lane_ok) ? x[u][j] : 0.0f;
+      }
+      float cm = m;
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) cm = __builtin_fmaxf(cm, sv[u]);
+      const float keep = guarded_exp2(m - cm);
+      z *= keep;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] *= keep;
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) {
+        const float w = guarded_exp2(sv[u] - cm);
+        z += w;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = (w > 0.0f) ? __builtin_fmaf(w, x[u][j], acc[j]) : acc[j];
+      }
+      m = cm;
     }
   }
 
@@ -159,22 +187,39 @@ hipError_t merge_state_out(int dt_out, const void* va, const float* sa, const vo
   return hipGetLastError();
 }
 
-template <int DTI>
-hipError_t merge_states_out(int dt_out, const void* v, const float* s, void* vo, float* so,
-                            int64_t rows, int N, int H, int D, int lanes_shift, int groups_shift,
-                            dim3 grid, hipStream_t st) {
-  switch (dt_out) {
-    case MI_F16:
-      merge_states_kernel<DTI, MI_F16><<<grid, kBlock, 0, st>>>(v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift);
+template <int DTI, int DTO>
+hipError_t merge_states_chunk(int chunk, const void* v, const float* s, void* vo, float* so,
+                              int64_t rows, int N, int H, int D, int lanes_shift,
+                              int groups_shift, dim3 grid, hipStream_t st) {
+  switch (chunk) {
+    case 1:
+      merge_states_kernel<DTI, DTO, 1><<<grid, kBlock, 0, st>>>(v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift);
       break;
-    case MI_BF16:
-      merge_states_kernel<DTI, MI_BF16><<<grid, kBlock, 0, st>>>(v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift);
+    case 2:
+      merge_states_kernel<DTI, DTO, 2><<<grid, kBlock, 0, st>>>(v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift);
+      break;
+    case 4:
+      merge_states_kernel<DTI, DTO, 4><<<grid, kBlock, 0, st>>>(v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift);
       break;
     default:
-      merge_states_kernel<DTI, MI_F32><<<grid, kBlock, 0, st>>>(v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift);
+      merge_states_kernel<DTI, DTO, 8><<<grid, kBlock, 0, st>>>(v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift);
       break;
   }
   return hipGetLastError();
+}
+
+template <int DTI>
+hipError_t merge_states_out(int dt_out, int chunk, const void* v, const float* s, void* vo,
+                            float* so, int64_t rows, int N, int H, int D, int lanes_shift,
+                            int groups_shift, dim3 grid, hipStream_t st) {
+  switch (dt_out) {
+    case MI_F16:
+      return merge_states_chunk<DTI, MI_F16>(chunk, v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift, grid, st);
+    case MI_BF16:
+      return merge_states_chunk<DTI, MI_BF16>(chunk, v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift, grid, st);
+    default:
+      return merge_states_chunk<DTI, MI_F32>(chunk, v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift, grid, st);
+  }
 }
 
 }  // namespace
@@ -199,16 +244,20 @@ hipError_t launch_merge_states(const void* v, const float* s, void* vo, float* s
   const int lanes_shift = log2_int(L);
   // Split the N states of a row over G lane groups when rows alone would not
   // give the device enough independent loads in flight.
-  constexpr int64_t kTargetThreads = 64 * 1024;
+  constexpr int64_t kTargetThreads = 16 * 1024;
   int G = 1;
   while (G < N && G * L < kBlock && rows * L * G < kTargetThreads) G *= 2;
   const int groups_shift = log2_int(G);
+  // States per group per chunk: enough to cover a group's share in one pass
+  // when it is small, at most 8.
+  const int per_group = (N + G - 1) / G;
+  const int chunk = per_group >= 8 ? 8 : next_pow2(per_group);
   const int64_t rows_per_block = kBlock >> (lanes_shift + groups_shift);
   const dim3 grid(static_cast<unsigned>((rows + rows_per_block - 1) / rows_per_block));
   switch (dt_in) {
-    case MI_F16: return merge_states_out<MI_F16>(dt_out, v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift, grid, st);
-    case MI_BF16: return merge_states_out<MI_BF16>(dt_out, v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift, grid, st);
-    default: return merge_states_out<MI_F32>(dt_out, v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift, grid, st);
+    case MI_F16: return merge_states_out<MI_F16>(dt_out, chunk, v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift, grid, st);
+    case MI_BF16: return merge_states_out<MI_BF16>(dt_out, chunk, v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift, grid, st);
+    default: return merge_states_out<MI_F32>(dt_out, chunk, v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift, grid, st);
   }
 }
 

@@ -187,3 +187,25 @@ def test_plan_and_range_validation():
     assert lib.mi_split_range(10, 16, 4, 4, ctypes.byref(a), ctypes.byref(b)) == ESHAPE
     assert lib.mi_split_range(-1, 16, 4, 0, ctypes.byref(a), ctypes.byref(b)) == ESHAPE
     assert lib.mi_split_range(10, 16, 4, 0, None, ctypes.byref(b)) == ENULL
+
+
+def test_fused_decode_validation():
+    lib = mi.lib()
+
+    def call(**kw):
+        a = dict(q=P(0), k=P(1 << 30), v=P(2 << 30), pt=P(3 << 30), ctx=P(4 << 30),
+                 op=P(5 << 30), lp=P(6 << 30), cnt=P(9 << 30), o=P(7 << 30), lse=P(8 << 30),
+                 dto=F16, B=2, splits=4)
+        a.update(kw)
+        return lib.mi_split_kv_decode_fused(a["q"], a["k"], a["v"], a["pt"], 64, a["ctx"], a["B"],
+                                            32, 8, 128, 16, 1024, a["splits"], ctypes.c_float(0.1),
+                                            F16, a["op"], a["lp"], a["cnt"], a["o"], a["lse"],
+                                            a["dto"], NULL)
+    assert call(cnt=NULL) == ENULL
+    assert call(o=NULL) == ENULL
+    assert call(cnt=P((7 << 30) + 64)) == EALIAS    # counters inside o
+    assert call(cnt=P((1 << 30) + 4)) == EALIAS     # counters inside the K cache
+    assert call(cnt=P(2)) == EUNSUP                  # misaligned
+    assert call(dto=5) == EDTYPE
+    assert call(splits=0) == ESHAPE
+    assert call(B=0) == OK

@@ -152,3 +152,87 @@ def test_split_count_invariance():
         out, lse, _, _ = _decode(case, splits, torch.float32)
         check_values(out, o)
         check_lse(lse, s)
+
+
+# ----------------------------------------------------------------------------- single launch
+
+def _decode_fused(case, splits, out_dtype=None, counters=None):
+    q, k, v, pt, ctx = _dev(case)
+    B, Hq, D = q.shape
+    Hkv = case["Hkv"]
+    nan = float("nan")
+    if counters is None:
+        counters = torch.zeros((B, Hkv), dtype=torch.int32, device="cuda")
+    o_part = torch.full((B, Hq, splits, D), nan, dtype=torch.float32, device="cuda")
+    lse_part = torch.full((B, Hq, splits), nan, dtype=torch.float32, device="cuda")
+    odt = out_dtype or q.dtype
+    out = torch.full((B, Hq, D), nan, dtype=odt, device="cuda")
+    lse = torch.full((B, Hq), nan, dtype=torch.float32, device="cuda")
+    mi.split_kv_decode_fused(q, k, v, pt, ctx, splits, case["sm_scale"], counters=counters,
+                             o_part=o_part, lse_part=lse_part, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert int(counters.abs().sum()) == 0, "counters must be left at zero"
+    return out, lse, o_part, lse_part
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("Hq,Hkv", [(4, 1), (32, 8), (16, 2), (8, 8)])
+@pytest.mark.parametrize("splits", [1, 4, 64, 100])
+def test_fused_decode_small_ragged(dtype, Hq, Hkv, splits):
+    _say("fused decode small", dtype, Hq, Hkv, splits)
+    ctx = np.array([1, 16, 17, 37, 100, 0, 250, 1000, 129], np.int32)
+    case = inputs.paged_kv_case(400 + Hq + splits, ctx, Hq, Hkv, 128, 16, dtype=dtype,
+                                extra_pages=5)
+    out, lse, o_part, lse_part = _decode_fused(case, splits)
+    o, s, op, sp = _oracle(case, splits)
+    check_values(o_part, op, "o_part")
+    check_lse(lse_part, sp, "lse_part")
+    check_values(out, o, "o")
+    check_lse(lse, s, "lse")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16, torch.float16])
+def test_fused_decode_output_dtypes(out_dtype):
+    _say("fused decode out dtype", out_dtype)
+    ctx = np.array([33, 700, 4], np.int32)
+    case = inputs.paged_kv_case(43, ctx, 8, 2, 128, 16, dtype="f16")
+    out, lse, _, _ = _decode_fused(case, 4, out_dtype)
+    o, s, _, _ = _oracle(case, 4)
+    check_values(out, o)
+    check_lse(lse, s)
+
+
+def test_fused_decode_long_context_and_mixed_batch():
+    """The B=1 ctx=32768 64-split case and the mixed batch through the single
+    launch; repeated calls reuse the counters and give the same bits."""
+    _say("fused decode long + mixed")
+    ctx = np.array([32768], np.int32)
+    case = inputs.paged_kv_case(1003, ctx, 32, 8, 128, 16, dtype="f16")
+    counters = torch.zeros((1, 8), dtype=torch.int32, device="cuda")
+    out1, lse1, _, _ = _decode_fused(case, 64, counters=counters)
+    out2, lse2, _, _ = _decode_fused(case, 64, counters=counters)
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse1.view(torch.int32), lse2.view(torch.int32))
+    o, s, _, _ = _oracle(case, 64)
+    check_values(out1, o)
+    check_lse(lse1, s)
+    ctx = inputs.mixed_ctx_lens(1004, 32)
+    case = inputs.paged_kv_case(1004, ctx, 32, 8, 128, 16, dtype="f16")
+    splits = mi.plan_splits(ctx, 8, 16)
+    out, lse, _, _ = _decode_fused(case, splits)
+    o, s, _, _ = _oracle(case, splits)
+    check_values(out, o)
+    check_lse(lse, s)
+
+
+def test_fused_matches_two_launch_decode():
+    _say("fused vs two-launch")
+    ctx = np.array([5000, 3, 64, 999], np.int32)
+    case = inputs.paged_kv_case(81, ctx, 32, 8, 128, 16, dtype="bf16")
+    a = _decode(case, 16, torch.float32)
+    b = _decode_fused(case, 16, torch.float32)
+    # identical pass 1; the two combines differ only in summation order
+    assert torch.equal(a[2].view(torch.int32), b[2].view(torch.int32))
+    assert torch.equal(a[3].view(torch.int32), b[3].view(torch.int32))
+    assert torch.allclose(a[0], b[0], rtol=1e-5, atol=1e-6)
+    assert torch.allclose(a[1], b[1], rtol=0, atol=1e-5)
