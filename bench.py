@@ -6,7 +6,10 @@ A step runs, on synthetic data resident in HBM:
                    layout of the S=64 parity case at a size that streams HBM)
   3. split-KV decode fp16 B=1, ctx=32768, Hq=32, Hkv=8, D=128, PAGE=16: the
                    planner picks the split count (64), then pass 1 and the
-                   combine (the two launches mi_split_kv_decode makes)
+                   combine in one launch (mi_split_kv_decode_fused)
+  4. cascade bf16: 64 requests share an 8192-token prefix (matrix-core level),
+                   each has a 512-token suffix (split-KV decode), then the two
+                   levels are merged with merge_state
 Inputs are rotated across copies so that consecutive uses of one buffer are
 separated by far more traffic than the 256 MB Infinity Cache holds.
 
@@ -194,7 +197,56 @@ def build_workload(torch, mi, inputs):
                       bytes=dec_partial_bytes + dec_combine_bytes, run=run_decode, host=plan,
                       shape=(f"f16 B=1 ctx=32768 Hq=32 Hkv=8 D=128 PAGE=16 splits={splits}, "
                              "pass 1 and combine in one launch")))
+    # 4. cascade, bf16: 64 requests share an 8192-token prefix, 512-token suffixes
+    cas = inputs.cascade_case(1005)
+    R, cHq, cHkv = cas["R"], cas["Hq"], cas["Hkv"]
+    cq = to_dev(cas["q"], "bf16", torch)
+    ck, cv = to_dev(cas["k"], "bf16", torch), to_dev(cas["v"], "bf16", torch)
+    cpages = torch.from_numpy(cas["prefix_pages"]).cuda()
+    ctab = torch.from_numpy(cas["suffix_table"]).cuda()
+    clen = torch.from_numpy(cas["suffix_lens"]).cuda()
+    cP = cas["k"].shape[0]
+    c_splits = mi.plan_splits(cas["suffix_lens"], cHkv, 16)
+    ws_bytes = mi.prefix_attention_workspace_bytes(R, cHq, cHkv, 128, cas["prefix_len"])
+    c_ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device="cuda")
+    vp = torch.empty((R, cHq, 128), dtype=torch.float32, device="cuda")
+    sp = torch.empty((R, cHq), dtype=torch.float32, device="cuda")
+    vs = torch.empty_like(vp)
+    ss = torch.empty_like(sp)
+    c_op = torch.empty((R, cHq, c_splits, 128), dtype=torch.float32, device="cuda")
+    c_lp = torch.empty((R, cHq, c_splits), dtype=torch.float32, device="cuda")
+    c_cnt = torch.zeros((R, cHkv), dtype=torch.int32, device="cuda")
+    c_o = torch.empty((R, cHq, 128), dtype=torch.bfloat16, device="cuda")
+    c_lse = torch.empty((R, cHq), dtype=torch.float32, device="cuda")
+    cscale = float(cas["sm_scale"])
+    prefix_call = Raw(mi, "mi_prefix_attention", cq, ck, cv, cpages, cas["prefix_len"], R, cHq,
+                      cHkv, 128, 16, cP, cscale, mi.MI_BF16, c_ws, ws_bytes, vp, sp, mi.MI_F32, st)
+    suffix_call = Raw(mi, "mi_split_kv_decode_fused", cq, ck, cv, ctab, ctab.shape[1], clen, R,
+                      cHq, cHkv, 128, 16, cP, c_splits, cscale, mi.MI_BF16, c_op, c_lp, c_cnt, vs,
+                      ss, mi.MI_F32, st)
+    level_merge = Raw(mi, "mi_merge_state", vp, sp, vs, ss, c_o, c_lse, R * cHq, 1, 128,
+                      mi.MI_F32, mi.MI_BF16, st)
+    n_ch = ws_bytes // (R * cHq * 129 * 4)
+    rows_s = R * cHq
+    prefix_bytes = (cas["prefix_len"] * cHkv * 128 * 2 * 2 + cq.numel() * 2 + cpages.numel() * 4
+                    + 2 * rows_s * n_ch * 129 * 4 + rows_s * 129 * 4)
+    suffix_bytes = (R * 512 * cHkv * 128 * 2 * 2 + cq.numel() * 2 + ctab.numel() * 4 + R * 4
+                    + 2 * rows_s * c_splits * 129 * 4 + rows_s * 129 * 4)
+    merge_bytes = 2 * rows_s * 129 * 4 + rows_s * (128 * 2 + 4)
+    prefix_flops = 4 * R * cHq * cas["prefix_len"] * 128
+
+    def run_cascade(i):
+        prefix_call()
+        suffix_call()
+        level_merge()
+
+    parts.append(dict(name="cascade", kernel="prefix_attention_kernel",
+                      bytes=prefix_bytes + suffix_bytes + merge_bytes, run=run_cascade,
+                      shape=("bf16 64 requests, shared prefix 8192 + suffix 512, Hq=32 Hkv=8 "
+                             f"D=128; prefix on MFMA ({n_ch} chunks), suffix splits={c_splits}")))
+
     host = dict(ms=ms, mss=mss, dec=dec, splits=splits, decode_calls=decode_calls,
+                prefix_call=prefix_call, prefix_flops=prefix_flops, prefix_bytes=prefix_bytes,
                 fused_calls=fused_calls, partial_calls=partial_calls, combine_call=combine_call,
                 plan=plan)
     return parts, host
@@ -287,6 +339,11 @@ def main():
             timer.stop(label)
         torch.cuda.synchronize()
     for i in range(args.steps):
+        timer.start("prefix")
+        host["prefix_call"]()
+        timer.stop("prefix")
+    torch.cuda.synchronize()
+    for i in range(args.steps):
         timer.start("split_kv_partial")
         host["partial_calls"][i % 4]()
         timer.stop("split_kv_partial")
@@ -322,7 +379,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": ("merge_state bf16 S=32768 H=32 D=128 + merge_states f16 "
                                 "S=65536 N=4 H=8 D=128 + split-KV decode f16 B=1 ctx=32768 "
-                                f"Hq=32 Hkv=8 D=128 PAGE=16 splits={host['splits']}"),
+                                f"Hq=32 Hkv=8 D=128 PAGE=16 splits={host['splits']} + cascade "
+                                "bf16 64 x (8192 shared + 512) Hq=32 Hkv=8 D=128"),
                    "step_bytes": step_bytes},
         "frac_of_peak": round(value / HBM_PEAK_GBS, 4),
         "gpu_ms_per_step": round(gpu_ms_per_step, 4),
@@ -331,6 +389,10 @@ def main():
         "decode_two_launch_us": round(timer.mean_us("decode_two_launch"), 2),
         "decode_pass1_us": round(timer.mean_us("split_kv_partial"), 2),
         "decode_combine_us": round(timer.mean_us("combine"), 2),
+        "cascade_prefix": {"us": round(timer.mean_us("prefix"), 2),
+                           "TFLOP/s": round(host["prefix_flops"] / (timer.mean_us("prefix") * 1e-6) / 1e12, 1),
+                           "mfma_peak_TFLOP/s": 2500.0,
+                           "GB/s": round(host["prefix_bytes"] / (timer.mean_us("prefix") * 1e-6) / 1e9, 1)},
         "kernels": per,
         "roofline": roofline,
     }

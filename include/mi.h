@@ -173,6 +173,37 @@ mi_status mi_split_kv_decode_fused(const void* q, const void* k_cache, const voi
                                    float* o_part, float* lse_part, int32_t* counters, void* o,
                                    float* lse, mi_dtype out_dtype, void* stream);
 
+/*
+ * Cascade level 0 ("F2 hints: merge_state, base-2 LSE merge", section 6): R
+ * requests share one prefix; the prefix's K/V is read once and every request's
+ * query heads attend to it together as dense matrix products on the matrix
+ * cores. Produces each (request, query head)'s prefix state, to be merged with
+ * its suffix state (mi_split_kv_decode*, then mi_merge_state).
+ *   q            : [R, Hq, D] of kv_dtype
+ *   k_cache,
+ *   v_cache      : [num_phys_pages, Hkv, page_size, D] of kv_dtype
+ *   prefix_pages : [ceil(prefix_len / page_size)] int32 (device), the prefix's
+ *                  physical pages in order; ids outside [0, num_phys_pages)
+ *                  contribute no tokens
+ *   workspace    : fp32 device buffer of at least the size reported by
+ *                  mi_prefix_attention_workspace (chunk partial states)
+ *   v_out        : [R, Hq, D] of out_dtype;  s_out : [R, Hq] fp32 base 2 (may be NULL)
+ * Query head hq uses kv head hq / (Hq / Hkv); scores are sm_scale * q.k.
+ * prefix_len = 0 gives the empty state (0, -inf). Supported: D = 128,
+ * page_size = 16, kv_dtype f16 or bf16. Two launches on `stream` (the chunked
+ * contraction, then the merge of the chunk states).
+ */
+mi_status mi_prefix_attention(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* prefix_pages, int32_t prefix_len, int32_t R,
+                              int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size,
+                              int64_t num_phys_pages, float sm_scale, mi_dtype kv_dtype,
+                              float* workspace, size_t ws_bytes, void* v_out, float* s_out,
+                              mi_dtype out_dtype, void* stream);
+
+/* Workspace bytes mi_prefix_attention needs for this shape (host only). */
+mi_status mi_prefix_attention_workspace(int32_t R, int32_t Hq, int32_t Hkv, int32_t D,
+                                        int32_t prefix_len, size_t* ws_bytes);
+
 #ifdef __cplusplus
 }
 #endif

@@ -40,6 +40,9 @@ SIGNATURES = {
                            ctypes.c_int, _P, _P, _P, _P, ctypes.c_int, _P],
     "mi_split_kv_decode_fused": [_P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I64,
                                  _I32, _F, ctypes.c_int, _P, _P, _P, _P, _P, ctypes.c_int, _P],
+    "mi_prefix_attention": [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I64, _F,
+                            ctypes.c_int, _P, ctypes.c_size_t, _P, _P, ctypes.c_int, _P],
+    "mi_prefix_attention_workspace": [_I32, _I32, _I32, _I32, _I32, _P],
 }
 
 
@@ -249,3 +252,49 @@ def split_kv_decode_fused(q, k_cache, v_cache, page_table, ctx_lens, num_splits:
     if return_partials:
         return out, lse, o_part, lse_part
     return out, lse
+
+
+# ----------------------------------------------------------------------------- cascade
+
+def prefix_attention_workspace_bytes(R: int, Hq: int, Hkv: int, D: int, prefix_len: int) -> int:
+    out = ctypes.c_size_t()
+    _call("mi_prefix_attention_workspace", R, Hq, Hkv, D, prefix_len, ctypes.byref(out))
+    return out.value
+
+
+def prefix_attention(q, k_cache, v_cache, prefix_pages, prefix_len: int, sm_scale: float,
+                     out_dtype=torch.float32, workspace=None, v_out=None, s_out=None):
+    """Cascade level 0: every (request, head) of q [R, Hq, D] against the shared
+    prefix pages -> (v [R, Hq, D] out_dtype, s [R, Hq] f32 base 2)."""
+    _check_cuda(q, k_cache, v_cache, prefix_pages, v_out, s_out)
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q must be [R, Hq, D] and k/v caches [pages, Hkv, PAGE, D]")
+    if prefix_pages.dtype != torch.int32:
+        raise TypeError("prefix_pages must be int32")
+    R, Hq, D = q.shape
+    P, Hkv, page, _ = k_cache.shape
+    need = prefix_attention_workspace_bytes(R, Hq, Hkv, D, prefix_len)
+    if workspace is None:
+        workspace = torch.empty(max(need // 4, 1), dtype=torch.float32, device=q.device)
+    if v_out is None:
+        v_out = torch.empty((R, Hq, D), dtype=out_dtype, device=q.device)
+    if s_out is None:
+        s_out = torch.empty((R, Hq), dtype=torch.float32, device=q.device)
+    _check_cuda(workspace)
+    _call("mi_prefix_attention", _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(prefix_pages),
+          prefix_len, R, Hq, Hkv, D, page, P, float(sm_scale), _dt(q), _ptr(workspace),
+          workspace.numel() * 4, _ptr(v_out), _ptr(s_out), _dt(v_out), _stream(q))
+    return v_out, s_out
+
+
+def cascade_decode(q, k_cache, v_cache, prefix_pages, prefix_len: int, suffix_table,
+                   suffix_lens, sm_scale: float, suffix_splits: int = 1, out_dtype=None):
+    """Two-level cascade decode: the shared prefix level (matrix cores), each
+    request's own suffix (split-KV decode), then the merge of the two states.
+    Returns (o [R, Hq, D], lse [R, Hq]) and the per-level states."""
+    out_dtype = out_dtype or q.dtype
+    vp, sp = prefix_attention(q, k_cache, v_cache, prefix_pages, prefix_len, sm_scale)
+    vs, ss = split_kv_decode_fused(q, k_cache, v_cache, suffix_table, suffix_lens, suffix_splits,
+                                   sm_scale, out_dtype=torch.float32)
+    o, lse = merge_state(vp, sp, vs, ss, out_dtype=out_dtype)
+    return o, lse, (vp, sp), (vs, ss)

@@ -306,4 +306,67 @@ mi_status mi_split_kv_decode_fused(const void* q, const void* k_cache, const voi
                                               out_dtype));
 }
 
+mi_status mi_prefix_attention_workspace(int32_t R, int32_t Hq, int32_t Hkv, int32_t D,
+                                        int32_t prefix_len, size_t* ws_bytes) {
+  if (!ws_bytes) return MI_ERR_NULL;
+  if (R < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || prefix_len < 0)
+    return MI_ERR_SHAPE;
+  if (D != 128) return MI_ERR_UNSUPPORTED;
+  int n_chunks, chunk_tokens;
+  mi::prefix_attention_plan(R > 0 ? R : 1, Hq, Hkv, prefix_len, &n_chunks, &chunk_tokens);
+  *ws_bytes = static_cast<size_t>(R) * Hq * n_chunks * (D + 1) * sizeof(float);
+  return MI_OK;
+}
+
+mi_status mi_prefix_attention(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* prefix_pages, int32_t prefix_len, int32_t R,
+                              int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size,
+                              int64_t num_phys_pages, float sm_scale, mi_dtype kv_dtype,
+                              float* workspace, size_t ws_bytes, void* v_out, float* s_out,
+                              mi_dtype out_dtype, void* stream) {
+  if (!q || !k_cache || !v_cache || !workspace || !v_out) return MI_ERR_NULL;
+  if (prefix_len > 0 && !prefix_pages) return MI_ERR_NULL;
+  if (R < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || page_size <= 0 ||
+      prefix_len < 0 || num_phys_pages <= 0)
+    return MI_ERR_SHAPE;
+  if (kv_dtype != MI_F16 && kv_dtype != MI_BF16) return MI_ERR_DTYPE;
+  if (!dtype_ok(out_dtype)) return MI_ERR_DTYPE;
+  if (D != 128 || page_size != 16) return MI_ERR_UNSUPPORTED;
+  if (!size_ok(num_phys_pages, Hkv, static_cast<int64_t>(page_size) * D, 2) ||
+      !size_ok(R, Hq, D, 4))
+    return MI_ERR_SHAPE;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(workspace, 16) || !aligned(v_out, 16) || !aligned(s_out, 4) ||
+      !aligned(prefix_pages, 4))
+    return MI_ERR_UNSUPPORTED;
+  size_t need = 0;
+  mi_status st = mi_prefix_attention_workspace(R, Hq, Hkv, D, prefix_len, &need);
+  if (st != MI_OK) return st;
+  if (ws_bytes < need) return MI_ERR_SHAPE;
+  const int64_t q_b = int64_t(R) * Hq * D * 2;
+  const int64_t cache_b = num_phys_pages * Hkv * page_size * D * 2;
+  const int64_t pp_b = int64_t(mi::ceil_div(prefix_len, page_size)) * 4;
+  const int64_t vo_b = int64_t(R) * Hq * D * dtype_bytes(out_dtype);
+  const int64_t so_b = int64_t(R) * Hq * 4;
+  const int64_t ws_b = static_cast<int64_t>(need);
+  const void* ins[4] = {q, k_cache, v_cache, prefix_pages};
+  const int64_t in_b[4] = {q_b, cache_b, cache_b, pp_b};
+  for (int i = 0; i < 4; ++i)
+    if (overlaps(workspace, ws_b, ins[i], in_b[i]) || overlaps(v_out, vo_b, ins[i], in_b[i]) ||
+        overlaps(s_out, so_b, ins[i], in_b[i]))
+      return MI_ERR_ALIAS;
+  if (overlaps(workspace, ws_b, v_out, vo_b) || overlaps(workspace, ws_b, s_out, so_b) ||
+      overlaps(v_out, vo_b, s_out, so_b))
+    return MI_ERR_ALIAS;
+  if (R == 0) return MI_OK;
+  int n_chunks, chunk_tokens;
+  mi::prefix_attention_plan(R, Hq, Hkv, prefix_len, &n_chunks, &chunk_tokens);
+  float* ws_o = workspace;
+  float* ws_s = workspace + static_cast<int64_t>(R) * Hq * n_chunks * D;
+  return from_hip(mi::launch_prefix_attention(q, k_cache, v_cache, prefix_pages, prefix_len, R,
+                                              Hq, Hkv, num_phys_pages, sm_scale, kv_dtype, ws_o,
+                                              ws_s, v_out, s_out, out_dtype,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

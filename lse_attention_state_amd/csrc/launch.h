@@ -21,4 +21,14 @@ hipError_t launch_split_kv_partial(const void* q, const void* kc, const void* vc
                                    hipStream_t stream, int32_t* counters = nullptr,
                                    void* o = nullptr, float* lse = nullptr, int out_dtype = -1);
 
+// Cascade prefix: chunk count and chunk length (tokens) for a shape.
+void prefix_attention_plan(int R, int Hq, int Hkv, int prefix_len, int* n_chunks,
+                           int* chunk_tokens);
+
+hipError_t launch_prefix_attention(const void* q, const void* kc, const void* vc,
+                                   const int32_t* prefix_pages, int prefix_len, int R, int Hq,
+                                   int Hkv, int64_t num_phys, float sm_scale, int kv_dtype,
+                                   float* ws_o, float* ws_s, void* v_out, float* s_out,
+                                   int out_dtype, hipStream_t stream);
+
 }  // namespace mi

@@ -1,0 +1,95 @@
+"""GPU parity of the cascade (shared-prefix) path against the fp64 oracle.
+
+Workload: 64 requests share an 8192-token prefix and each has its own
+512-token suffix, Hq=32, Hkv=8, D=128, PAGE=16, bf16, one shuffled page pool.
+The prefix level runs on the matrix cores, the suffixes through split-KV
+decode, and merge_state joins the levels; the result must equal unsplit
+attention over prefix + suffix. Smaller cases cover ragged prefix lengths,
+row counts that leave a partial row block, fp16, and the empty prefix.
+"""
+import numpy as np
+import pytest
+import torch
+
+import lse_attention_state_amd as mi
+import oracle
+from lse_attention_state_amd import inputs
+from parity import check_lse, check_values, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _prefix_oracle(case, prefix_len):
+    R = case["R"]
+    n_pre = -(-prefix_len // case["page"])
+    table = np.ascontiguousarray(np.broadcast_to(case["prefix_pages"][:n_pre], (R, n_pre)))
+    if n_pre == 0:
+        table = np.zeros((R, 1), np.int32)
+    lens = np.full(R, prefix_len, np.int32)
+    return oracle.attention(case["q"], case["k"], case["v"], table, lens, case["sm_scale"],
+                            case["dtype"], case["dtype"])
+
+
+def _dev(case):
+    dt = case["dtype"]
+    return to_device(case["q"], dt), to_device(case["k"], dt), to_device(case["v"], dt)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("R,Hq,Hkv,prefix_len", [(3, 8, 2, 100), (16, 32, 8, 1024),
+                                                 (5, 4, 1, 37), (20, 16, 2, 530),
+                                                 (7, 8, 8, 16)])
+def test_prefix_attention_small(dtype, R, Hq, Hkv, prefix_len):
+    _say("prefix small", dtype, R, Hq, Hkv, prefix_len)
+    case = inputs.cascade_case(900 + R + prefix_len, R=R, prefix_len=-(-prefix_len // 16) * 16,
+                               suffix_len=16, Hq=Hq, Hkv=Hkv, dtype=dtype)
+    q, k, v = _dev(case)
+    pages = torch.from_numpy(case["prefix_pages"]).cuda()
+    v_out = torch.full((R, Hq, 128), float("nan"), dtype=torch.float32, device="cuda")
+    s_out = torch.full((R, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    mi.prefix_attention(q, k, v, pages, prefix_len, case["sm_scale"], v_out=v_out, s_out=s_out)
+    torch.cuda.synchronize()
+    o, s = _prefix_oracle(case, prefix_len)
+    check_values(v_out, o)
+    check_lse(s_out, s)
+
+
+def test_prefix_attention_empty_prefix():
+    _say("prefix empty")
+    case = inputs.cascade_case(5, R=4, prefix_len=16, suffix_len=16, Hq=8, Hkv=2, dtype="bf16")
+    q, k, v = _dev(case)
+    pages = torch.from_numpy(case["prefix_pages"]).cuda()
+    vo, so = mi.prefix_attention(q, k, v, pages, 0, case["sm_scale"])
+    torch.cuda.synchronize()
+    assert torch.all(vo == 0) and torch.all(so == float("-inf"))
+
+
+def test_cascade_64_requests_8k_prefix_512_suffix():
+    _say("cascade full")
+    case = inputs.cascade_case(1005)
+    q, k, v = _dev(case)
+    pages = torch.from_numpy(case["prefix_pages"]).cuda()
+    st = torch.from_numpy(case["suffix_table"]).cuda()
+    sl = torch.from_numpy(case["suffix_lens"]).cuda()
+    splits = mi.plan_splits(case["suffix_lens"], 8, 16)
+    o, lse, (vp, sp), (vs, ss) = mi.cascade_decode(q, k, v, pages, case["prefix_len"], st, sl,
+                                                   case["sm_scale"], suffix_splits=splits)
+    torch.cuda.synchronize()
+    # the final result against unsplit attention over prefix + suffix
+    ro, rs = oracle.attention(case["q"], case["k"], case["v"], case["full_table"],
+                              case["full_lens"], case["sm_scale"], "bf16", "bf16")
+    stats = check_values(o, ro)
+    check_lse(lse, rs)
+    # each level against its own definition
+    po, ps = _prefix_oracle(case, case["prefix_len"])
+    check_values(vp, po, "prefix v")
+    check_lse(sp, ps, "prefix s")
+    so_, ss_ = oracle.attention(case["q"], case["k"], case["v"], case["suffix_table"],
+                                case["suffix_lens"], case["sm_scale"], "bf16", "bf16")
+    check_values(vs, so_, "suffix v")
+    check_lse(ss, ss_, "suffix s")
+    _say("cascade stats", stats, "suffix splits", splits)
