@@ -34,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "HBM GB/s (% of peak) for merge_states + split-KV decode µs at B=1 ctx=32K"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
@@ -103,6 +104,26 @@ class Timer:
 
     def reset(self):
         self.pairs = {}
+
+
+def counter_traffic(name):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE passes,
+    or None when there are none for this kernel or its sources have changed
+    since the counters were taken (a stored hash of the sources decides)."""
+    import hashlib
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    with open(COUNTERS_FILE) as f:
+        tr = json.load(f).get(name)
+    if tr is None:
+        return None
+    h = hashlib.sha256()
+    for src in tr["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest()[:16] != tr["sources_sha256_16"]:
+        return None
+    return tr["bytes_per_launch"]
 
 
 def build_workload(torch, mi, inputs):
@@ -235,15 +256,16 @@ def build_workload(torch, mi, inputs):
     merge_bytes = 2 * rows_s * 129 * 4 + rows_s * (128 * 2 + 4)
     prefix_flops = 4 * R * cHq * cas["prefix_len"] * 128
 
-    def run_cascade(i):
-        prefix_call()
-        suffix_call()
-        level_merge()
-
-    parts.append(dict(name="cascade", kernel="prefix_attention_kernel",
-                      bytes=prefix_bytes + suffix_bytes + merge_bytes, run=run_cascade,
-                      shape=("bf16 64 requests, shared prefix 8192 + suffix 512, Hq=32 Hkv=8 "
-                             f"D=128; prefix on MFMA ({n_ch} chunks), suffix splits={c_splits}")))
+    parts.append(dict(name="cascade_prefix", kernel="prefix_attention_kernel", bytes=prefix_bytes,
+                      flops=prefix_flops, run=lambda i: prefix_call(),
+                      shape=(f"bf16 64 requests x shared prefix 8192, Hq=32 Hkv=8 D=128, MFMA, "
+                             f"{n_ch} chunks + chunk merge")))
+    parts.append(dict(name="cascade_suffix", kernel="split_kv_partial_kernel", bytes=suffix_bytes,
+                      run=lambda i: suffix_call(),
+                      shape=f"bf16 64 requests x suffix 512, splits={c_splits}, single launch"))
+    parts.append(dict(name="cascade_merge", kernel="merge_state_kernel", bytes=merge_bytes,
+                      run=lambda i: level_merge(),
+                      shape="f32 prefix and suffix states [64, 32, 128] -> bf16"))
 
     host = dict(ms=ms, mss=mss, dec=dec, splits=splits, decode_calls=decode_calls,
                 prefix_call=prefix_call, prefix_flops=prefix_flops, prefix_bytes=prefix_bytes,
@@ -339,11 +361,6 @@ def main():
             timer.stop(label)
         torch.cuda.synchronize()
     for i in range(args.steps):
-        timer.start("prefix")
-        host["prefix_call"]()
-        timer.stop("prefix")
-    torch.cuda.synchronize()
-    for i in range(args.steps):
         timer.start("split_kv_partial")
         host["partial_calls"][i % 4]()
         timer.stop("split_kv_partial")
@@ -358,16 +375,14 @@ def main():
     for p in parts:
         us = timer.mean_us(p["name"])
         gbs = p["bytes"] / (us * 1e-6) / 1e9
-        per.append({"kernel": p["name"], "shape": p["shape"], "us": round(us, 2),
-                    "bytes": p["bytes"], "GB/s": round(gbs, 1),
-                    "frac": round(gbs / HBM_PEAK_GBS, 4)})
+        entry = {"kernel": p["name"], "shape": p["shape"], "us": round(us, 2),
+                 "bytes": p["bytes"], "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        if "flops" in p:
+            tf = p["flops"] / (us * 1e-6) / 1e12
+            entry.update({"TFLOP/s": round(tf, 1), "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)})
+        per.append(entry)
     dom = max(per, key=lambda r: r["us"])
-    traffic = None
-    if os.path.exists(COUNTERS_FILE):
-        with open(COUNTERS_FILE) as f:
-            tr = json.load(f).get(dom["kernel"])
-        if tr is not None:
-            traffic = tr.get("bytes_per_launch")
+    traffic = counter_traffic(dom["kernel"])
     roofline = {"bound": "hbm", "achieved": dom["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": dom["frac"], "traffic": traffic, "kernel": dom["kernel"]}
     decode_us = timer.mean_us("decode")
@@ -389,10 +404,6 @@ def main():
         "decode_two_launch_us": round(timer.mean_us("decode_two_launch"), 2),
         "decode_pass1_us": round(timer.mean_us("split_kv_partial"), 2),
         "decode_combine_us": round(timer.mean_us("combine"), 2),
-        "cascade_prefix": {"us": round(timer.mean_us("prefix"), 2),
-                           "TFLOP/s": round(host["prefix_flops"] / (timer.mean_us("prefix") * 1e-6) / 1e12, 1),
-                           "mfma_peak_TFLOP/s": 2500.0,
-                           "GB/s": round(host["prefix_bytes"] / (timer.mean_us("prefix") * 1e-6) / 1e9, 1)},
         "kernels": per,
         "roofline": roofline,
     }

@@ -273,6 +273,11 @@ mi_status mi_split_kv_decode(const void* q, const void* k_cache, const void* v_c
   if (st != MI_OK) return st;
   if (B == 0) return MI_OK;
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (num_splits == 1)  // one split: pass 1 writes o and lse itself, no combine launch
+    return from_hip(mi::launch_split_kv_partial(q, k_cache, v_cache, page_table, pt_stride,
+                                                ctx_lens, B, Hq, Hkv, num_phys_pages, 1, sm_scale,
+                                                kv_dtype, o_part, lse_part, s, nullptr, o, lse,
+                                                out_dtype));
   hipError_t e = mi::launch_split_kv_partial(q, k_cache, v_cache, page_table, pt_stride, ctx_lens,
                                              B, Hq, Hkv, num_phys_pages, num_splits, sm_scale,
                                              kv_dtype, o_part, lse_part, s);

@@ -27,11 +27,13 @@ constexpr int kPage = 16;
 constexpr int kBM = 64;              // query rows per workgroup
 constexpr int kBN = 32;              // prefix tokens per tile
 constexpr int kThreads = 256;
-constexpr int kVtStride = kBN + 8;   // padded row (elements) of the transposed V tile
-constexpr int kPStride = kBN + 8;    // padded row (elements) of a wave's P tile
-constexpr int kTileDepth = 4;        // tiles in flight per thread
+constexpr int kKStride = kD + 8;     // padded LDS row (elements) of the K tile
+constexpr int kVtStride = kBN + 8;   // padded LDS row (elements) of the transposed V tile
+constexpr int kPStride = kBN + 8;    // padded LDS row (elements) of a wave's P tile
+constexpr int kTileDepth = 3;        // tiles in flight per thread
+constexpr int kMaxChunkPages = 64;   // page ids of a chunk fit one VGPR of the wave
 constexpr int kBufferFlags = 0x00020000;
-constexpr int kTargetBlocks = 256;
+constexpr int kTargetBlocks = 512;   // two workgroups per compute unit
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -70,8 +72,9 @@ __global__ __launch_bounds__(kThreads) void prefix_attention_kernel(
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ prefix_pages, int prefix_len,
     int n_rows, int Hq, int Hkv, int G, int64_t num_phys, int chunk_tokens, int n_chunks,
     float qk_scale_log2, float* __restrict__ ws_o, float* __restrict__ ws_s) {
-  __shared__ __attribute__((aligned(16))) uint16_t ks[kBN * kD];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[kD * kVtStride];
+  // Double-buffered K (row-major) and V (transposed) tiles; per-wave P tiles.
+  __shared__ __attribute__((aligned(16))) uint16_t ks[2][kBN * kKStride];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[2][kD * kVtStride];
   __shared__ __attribute__((aligned(16))) uint16_t ps[4][16 * kPStride];
 
   // Block -> (row block, kv head, chunk). The row blocks of one (kv head,
@@ -88,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void prefix_attention_kernel(
   const int l16 = lane & 15;
   const int grp = lane >> 4;
 
-  // Q fragments (A operand): lane holds row wave*16 + l16, d = 32*ks + 8*grp + [0, 8).
+  // Q fragments (A operand): lane holds row wave*16 + l16, d = 32*k + 8*grp + [0, 8).
   u32x4_t qa[4];
   {
     const int r = rb * kBM + wave * 16 + l16;
@@ -106,28 +109,55 @@ __global__ __launch_bounds__(kThreads) void prefix_attention_kernel(
   tok1 = tok1 < prefix_len ? tok1 : prefix_len;
   const int n_tiles = tok1 > tok0 ? (tok1 - tok0 + kBN - 1) / kBN : 0;
   const int n_pages = (prefix_len + kPage - 1) / kPage;
+  const int page0 = tok0 / kPage;
 
-  // Tile loads: thread t covers slot t/16, d = 8*(t%16) of both pages of a tile.
-  const int slot = tid >> 4;
-  const int d8 = (tid & 15) * 8;
-  const int lane_bytes = tid * 16;
+  // The chunk's page ids, one per lane (a chunk spans at most 64 pages).
+  const int32_t ids = (page0 + lane < n_pages) ? prefix_pages[page0 + lane] : -1;
+
+  // Tile loads: wave w takes token rows 8w .. 8w+7 of the tile, i.e. half of
+  // page w/2, so each wave's buffer descriptor is uniform. Lane l takes the
+  // token pair 8w + 2(l%4), +1 at d = 8(l/4); a load instruction covers four
+  // whole 256-byte rows, and each lane can write V^T as packed token pairs.
+  const int pr = lane & 3;
+  const int c8 = (lane >> 2) * 8;
+  const int row0 = (wave & 1) * 8 + 2 * pr;            // token row within the page
+  const int lane_bytes = (row0 * kD + c8) * 2;
   const int64_t tile_elems = static_cast<int64_t>(kPage) * kD;
   u32x4_t kbuf[kTileDepth][2], vbuf[kTileDepth][2];
   auto issue = [&](int t, int j) {
+    const int pl = 2 * t + (wave >> 1);                 // page index within the chunk
+    const int32_t phys = __builtin_amdgcn_readlane(ids, pl & 63);
+    const bool ok = t < n_tiles && page0 + pl < n_pages && phys >= 0 && phys < num_phys;
+    const int64_t base = (static_cast<int64_t>(ok ? phys : 0) * Hkv + hkv) * tile_elems;
+    const int records = ok ? static_cast<int>(tile_elems * 2) : 0;
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kc + base), 0, records, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vc + base), 0, records, kBufferFlags);
+    kbuf[j][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, lane_bytes, 0, 0));
+    kbuf[j][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, lane_bytes + kD * 2, 0, 0));
+    vbuf[j][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, lane_bytes, 0, 0));
+    vbuf[j][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, lane_bytes + kD * 2, 0, 0));
+  };
+
+  // Stage tile t (registers slot j) into LDS buffer `buf`; tokens at or past
+  // the chunk end are zero in V (their scores are masked separately).
+  const int tk = 8 * wave + 2 * pr;                     // token pair within the tile
+  auto stage = [&](int t, int j, int buf) {
+    const int ttok = tok0 + t * kBN;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int page = (tok0 + t * kBN) / kPage + half;
-      const bool in = t < n_tiles && page < n_pages;
-      const int32_t phys = in ? prefix_pages[page] : -1;  // never read past the list
-      const bool ok = in && phys >= 0 && phys < num_phys;
-      const int64_t base = (static_cast<int64_t>(ok ? phys : 0) * Hkv + hkv) * tile_elems;
-      const int records = ok ? static_cast<int>(tile_elems * 2) : 0;
-      const __amdgpu_buffer_rsrc_t rk =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kc + base), 0, records, kBufferFlags);
-      const __amdgpu_buffer_rsrc_t rv =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vc + base), 0, records, kBufferFlags);
-      kbuf[j][half] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, lane_bytes, 0, 0));
-      vbuf[j][half] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, lane_bytes, 0, 0));
+    for (int h = 0; h < 2; ++h)
+      *reinterpret_cast<u32x4_t*>(&ks[buf][(tk + h) * kKStride + c8]) = kbuf[j][h];
+    const bool v0 = ttok + tk < tok1;
+    const bool v1 = ttok + tk + 1 < tok1;
+    const u32x4_t a = v0 ? vbuf[j][0] : u32x4_t{0, 0, 0, 0};
+    const u32x4_t b = v1 ? vbuf[j][1] : u32x4_t{0, 0, 0, 0};
+    uint32_t* vtw = reinterpret_cast<uint32_t*>(vt[buf]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t x = a[i], y = b[i];
+      vtw[((c8 + 2 * i) * kVtStride + tk) / 2] = (x & 0xffffu) | (y << 16);
+      vtw[((c8 + 2 * i + 1) * kVtStride + tk) / 2] = (x >> 16) | (y & 0xffff0000u);
     }
   };
 
@@ -141,38 +171,25 @@ __global__ __launch_bounds__(kThreads) void prefix_attention_kernel(
     lsum[e] = 0.0f;
   }
 
-  auto compute = [&](int t, int j) {
+  auto compute = [&](int t, int buf) {
     const int ttok = tok0 + t * kBN;
-    __syncthreads();  // the previous tile's LDS reads are done
-    // Stage K row-major and V transposed; tokens at or past the end are zero.
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int token = half * 16 + slot;
-      *reinterpret_cast<u32x4_t*>(ks + token * kD + d8) = kbuf[j][half];
-      const bool valid = ttok + token < tok1;
-      const u32x4_t vw = valid ? vbuf[j][half] : u32x4_t{0, 0, 0, 0};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t x = vw[i];
-        vt[(d8 + 2 * i) * kVtStride + token] = static_cast<uint16_t>(x & 0xffffu);
-        vt[(d8 + 2 * i + 1) * kVtStride + token] = static_cast<uint16_t>(x >> 16);
-      }
-    }
-    __syncthreads();
-
     // S = Q K^T for the wave's 16 rows and the tile's 32 tokens (two 16-column tiles).
     f32x4_t s[2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      s[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int c = 0; c < 2; ++c) s[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const u32x4_t kb = *reinterpret_cast<const u32x4_t*>(ks + (16 * c + l16) * kD + 32 * k + 8 * grp);
+    for (int k = 0; k < 4; ++k) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const u32x4_t kb = *reinterpret_cast<const u32x4_t*>(
+            &ks[buf][(16 * c + l16) * kKStride + 32 * k + 8 * grp]);
         s[c] = mfma16x16x32<DT>(qa[k], kb, s[c]);
       }
     }
     // Online softmax for the lane's rows 4*grp + e (columns 16c + l16).
     uint16_t pbits[2][4];
+    float alpha[4];
+    bool moved = false;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float x0 = s[0][e] * qk_scale_log2;
@@ -181,17 +198,22 @@ __global__ __launch_bounds__(kThreads) void prefix_attention_kernel(
       x1 = ttok + 16 + l16 < tok1 ? x1 : -kInf;
       const float mn = __builtin_fmaxf(m[e], row16_max(__builtin_fmaxf(x0, x1)));
       const float mu = mn == -kInf ? 0.0f : mn;
-      const float alpha = __builtin_amdgcn_exp2f(m[e] - mu);
+      alpha[e] = __builtin_amdgcn_exp2f(m[e] - mu);
+      moved |= mn != m[e];
       // The denominator takes the fp32 weights; only the P V product uses the
       // weights rounded to the input type (the LSE stays exact to fp32).
       const float p0 = __builtin_amdgcn_exp2f(x0 - mu);
       const float p1 = __builtin_amdgcn_exp2f(x1 - mu);
       pbits[0][e] = round16<DT>(p0);
       pbits[1][e] = round16<DT>(p1);
-      lsum[e] = lsum[e] * alpha + (p0 + p1);
+      lsum[e] = lsum[e] * alpha[e] + (p0 + p1);
       m[e] = mn;
+    }
+    if (__builtin_amdgcn_ballot_w64(moved) != 0) {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) o[c][e] *= alpha;
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o[c][e] *= alpha[e];
     }
     // P to LDS (row-major per wave), read back as the A operand of P V.
     uint16_t* pw = ps[wave];
@@ -203,22 +225,35 @@ __global__ __launch_bounds__(kThreads) void prefix_attention_kernel(
     const u32x4_t pa = *reinterpret_cast<const u32x4_t*>(pw + l16 * kPStride + 8 * grp);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const u32x4_t vb = *reinterpret_cast<const u32x4_t*>(vt + (16 * c + l16) * kVtStride + 8 * grp);
+      const u32x4_t vb = *reinterpret_cast<const u32x4_t*>(
+          &vt[buf][(16 * c + l16) * kVtStride + 8 * grp]);
       o[c] = mfma16x16x32<DT>(pa, vb, o[c]);
     }
   };
 
+  // Pipeline: registers hold tiles t+1 .. t+kTileDepth; tile t+1 is staged
+  // into the other LDS buffer while tile t is computed; one barrier per tile.
+  // The loop body is unconditional: tiles past the chunk end load zeros (no
+  // records) and have every score masked, so they change nothing, and the
+  // compiler can keep exact load counts across iterations.
 #pragma unroll
   for (int j = 0; j < kTileDepth; ++j) {
     issue(j, j);
     __builtin_amdgcn_sched_barrier(0);
   }
+  stage(0, 0, 0);
+  issue(kTileDepth, 0);
+  __syncthreads();
   const int iters = (n_tiles + kTileDepth - 1) / kTileDepth * kTileDepth;
   for (int base = 0; base < iters; base += kTileDepth) {
 #pragma unroll
     for (int j = 0; j < kTileDepth; ++j) {
-      if (base + j < n_tiles) compute(base + j, j);
-      issue(base + j + kTileDepth, j);
+      const int t = base + j;
+      const int jn = (j + 1) % kTileDepth;   // register slot of tile t+1
+      stage(t + 1, jn, (t + 1) & 1);
+      issue(t + 1 + kTileDepth, jn);
+      compute(t, t & 1);
+      __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -250,6 +285,7 @@ void prefix_attention_plan(int R, int Hq, int Hkv, int prefix_len, int* n_chunks
   c = c < 1 ? 1 : (c > max_chunks ? max_chunks : c);
   int tokens = prefix_len > 0 ? (prefix_len + c - 1) / c : kBN;
   tokens = (tokens + kBN - 1) / kBN * kBN;
+  if (tokens > kMaxChunkPages * kPage) tokens = kMaxChunkPages * kPage;
   *chunk_tokens = tokens;
   *n_chunks = prefix_len > 0 ? (prefix_len + tokens - 1) / tokens : 1;
 }

@@ -40,7 +40,7 @@ constexpr int kD = 128;
 constexpr int kPage = 16;
 // Pages in flight per wave, and page groups per workgroup (4 waves each).
 #ifndef MI_DECODE_DEPTH
-#define MI_DECODE_DEPTH 8
+#define MI_DECODE_DEPTH 4
 #endif
 #ifndef MI_DECODE_PAGE_GROUPS
 #define MI_DECODE_PAGE_GROUPS 1
@@ -52,6 +52,11 @@ constexpr int kThreads = 64 * kWaves;
 constexpr float kRescaleSlack = 8.0f;
 // Word 3 of a gfx9 buffer descriptor for raw (untyped, unswizzled) access.
 constexpr int kBufferFlags = 0x00020000;
+// Cache policy of the K/V loads (bit 1: non-temporal / streaming).
+#ifndef MI_DECODE_KV_POLICY
+#define MI_DECODE_KV_POLICY 2
+#endif
+constexpr int kKvCachePolicy = MI_DECODE_KV_POLICY;
 // s_waitcnt immediate (gfx9 encoding) for vmcnt(0), other counters unconstrained.
 constexpr int kWaitVmcnt0 = 0x0F70;
 
@@ -226,8 +231,8 @@ __global__ __launch_bounds__(kThreads) void split_kv_partial_kernel(
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kc + tile), 0, records, kBufferFlags);
     const __amdgpu_buffer_rsrc_t rv =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vc + tile), 0, records, kBufferFlags);
-    kb[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, lane_bytes, 0, 0));
-    vb[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, lane_bytes, 0, 0));
+    kb[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, lane_bytes, 0, kKvCachePolicy));
+    vb[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, lane_bytes, 0, kKvCachePolicy));
   };
 
   // Online softmax with a lazily updated reference max m[h]: exponentials are
@@ -362,6 +367,19 @@ __global__ __launch_bounds__(kThreads) void split_kv_partial_kernel(
     const float2 res = make_float2(o0 * inv, o1 * inv);
     const float lse_val = (Z > 0.0f) ? M + hw_log2(Z) : -kInf;
     if constexpr (DTO >= 0) {
+      if (num_splits == 1) {
+        // One split: the combine is the identity, so write the result directly.
+        *reinterpret_cast<float2*>(out) = res;
+        if (lane == 0) lse_part[row] = lse_val;
+        if constexpr (DTO == MI_F32) {
+          *reinterpret_cast<float2*>(static_cast<float*>(o) + row * kD + 2 * lane) = res;
+        } else {
+          const uint32_t w2 = DTO == MI_F16 ? pack_f16(res.x, res.y) : pack_bf16(res.x, res.y);
+          *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(o) + row * kD + 2 * lane) = w2;
+        }
+        if (lse != nullptr && lane == 0) lse[row] = lse_val;
+        continue;
+      }
       // Agent-scope stores are written through to the device coherence point,
       // so another XCD can read them without a writeback of this XCD's L2.
       __hip_atomic_store(reinterpret_cast<uint64_t*>(out), __builtin_bit_cast(uint64_t, res),
@@ -376,6 +394,7 @@ __global__ __launch_bounds__(kThreads) void split_kv_partial_kernel(
   }
 
   if constexpr (DTO >= 0) {
+    if (num_splits == 1) return;  // written directly above
     // Hand-off: every workgroup publishes its partials (agent-scope release)
     // and bumps the (sequence, kv head) counter; the one that brings it to
     // num_splits performs the acquire and merges all splits of its heads.
@@ -454,7 +473,9 @@ hipError_t launch_split_kv_partial(const void* q, const void* kc, const void* vc
   const dim3 grid(static_cast<unsigned>(num_splits), static_cast<unsigned>(Hkv),
                   static_cast<unsigned>(B));
   const float scale = static_cast<float>(static_cast<double>(sm_scale) * 1.4426950408889634);
-  const int dto = counters != nullptr ? out_dtype : -1;
+  // o is written by this kernel when fused (counters given) or when there is a
+  // single split (no combine needed); otherwise pass 1 only.
+  const int dto = (counters != nullptr || (o != nullptr && num_splits == 1)) ? out_dtype : -1;
   if (kv_dtype == MI_F16)
     return launch_dtype<MI_F16>(dto, G, grid, st, q, kc, vc, page_table, pt_stride, ctx_lens, Hkv,
                                 num_phys_pages, num_splits, scale, o_part, lse_part, counters, o,
