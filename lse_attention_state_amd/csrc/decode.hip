@@ -165,8 +165,10 @@ __global__ __launch_bounds__(kThreads) void split_kv_partial_kernel(
   __shared__ float lds_acc[kWaves][G][kD];
   __shared__ float lds_ml[kWaves][G][2];
 
-  const int split = blockIdx.x;
-  const int hkv = blockIdx.y;
+  // blockIdx.x is the kv head: consecutive workgroups go round-robin to the
+  // XCDs, so each kv head's splits stay on one XCD (and its L2).
+  const int hkv = blockIdx.x;
+  const int split = blockIdx.y;
   const int b = blockIdx.z;
   // The wave index is uniform across the wave: readfirstlane tells the
   // compiler so (it keeps wave-derived values in scalar registers).
@@ -192,10 +194,15 @@ __global__ __launch_bounds__(kThreads) void split_kv_partial_kernel(
   for (int h = 0; h < G; ++h)
     qw[h] = *reinterpret_cast<const u32x4_t*>(q + (static_cast<int64_t>(b) * Hq + hkv * G + h) * kD + d0);
 
-  float m[G], l[G], acc[G][8];
+  // m[h] is the reference max, mu[h] the value subtracted before exp2 (m, or
+  // 0 while m is -inf), thr[h] = m + kRescaleSlack; mu and thr change only
+  // when m does.
+  float m[G], mu[G], thr[G], l[G], acc[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m[h] = -kInf;
+    mu[h] = 0.0f;
+    thr[h] = -kInf;
     l[h] = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[h][j] = 0.0f;
@@ -250,15 +257,26 @@ __global__ __launch_bounds__(kThreads) void split_kv_partial_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = valid ? v[e] : 0.0f;
     }
+    // The G partial dots are reduced over the 16 lanes of a row step by step
+    // for all heads together, so the DPP steps of different heads interleave
+    // (a DPP read of a just-written VGPR otherwise needs wait states).
     float x[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) x[h] = dot8<DT>(qw[h], kb[j]);
+#pragma unroll
+    for (int h = 0; h < G; ++h) x[h] += dpp<kDppQuadXor1>(x[h]);
+#pragma unroll
+    for (int h = 0; h < G; ++h) x[h] += dpp<kDppQuadXor2>(x[h]);
+#pragma unroll
+    for (int h = 0; h < G; ++h) x[h] += dpp<kDppRowRor4>(x[h]);
+#pragma unroll
+    for (int h = 0; h < G; ++h) x[h] += dpp<kDppRowRor8>(x[h]);
     bool need_any = false;
     bool need[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      x[h] = row16_sum(dot8<DT>(qw[h], kb[j])) * qk_scale_log2;
-      if constexpr (kMasked) x[h] = valid ? x[h] : -kInf;
-      x[h] = page_ok ? x[h] : -kInf;
-      need[h] = x[h] > m[h] + kRescaleSlack;
+      x[h] = (valid && page_ok) ? x[h] * qk_scale_log2 : -kInf;
+      need[h] = x[h] > thr[h];
       need_any |= need[h];
     }
     if (__builtin_amdgcn_ballot_w64(need_any) != 0) {
@@ -266,6 +284,8 @@ __global__ __launch_bounds__(kThreads) void split_kv_partial_kernel(
       for (int h = 0; h < G; ++h) {
         const float alpha = need[h] ? __builtin_amdgcn_exp2f(m[h] - x[h]) : 1.0f;
         m[h] = need[h] ? x[h] : m[h];
+        mu[h] = (m[h] == -kInf) ? 0.0f : m[h];
+        thr[h] = m[h] + kRescaleSlack;
         l[h] *= alpha;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
@@ -273,8 +293,7 @@ __global__ __launch_bounds__(kThreads) void split_kv_partial_kernel(
     }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float mu = (m[h] == -kInf) ? 0.0f : m[h];
-      const float p = __builtin_amdgcn_exp2f(x[h] - mu);
+      const float p = __builtin_amdgcn_exp2f(x[h] - mu[h]);
       l[h] += p;
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[h][e] = __builtin_fmaf(p, v[e], acc[h][e]);
@@ -470,7 +489,7 @@ hipError_t launch_split_kv_partial(const void* q, const void* kc, const void* vc
                                    hipStream_t st, int32_t* counters, void* o, float* lse,
                                    int out_dtype) {
   const int G = Hq / Hkv;
-  const dim3 grid(static_cast<unsigned>(num_splits), static_cast<unsigned>(Hkv),
+  const dim3 grid(static_cast<unsigned>(Hkv), static_cast<unsigned>(num_splits),
                   static_cast<unsigned>(B));
   const float scale = static_cast<float>(static_cast<double>(sm_scale) * 1.4426950408889634);
   // o is written by this kernel when fused (counters given) or when there is a
