@@ -5,17 +5,32 @@
 //
 // For one kv head, the query rows are the (request, query head) pairs that use
 // it: row r = req * G + g reads q[req, hkv * G + g, :]. One workgroup takes a
-// block of 64 rows (16 per wave) and one chunk of the prefix, and runs an
-// online softmax over the chunk in tiles of 32 tokens (two pages):
-//   S = Q K^T     v_mfma_f32_16x16x32 (A = Q from registers, B = K from LDS)
-//   P = 2^(S*scale*log2e - m)  (rounded to the input type for the next product;
-//                               the softmax denominator uses the fp32 values)
-//   O += P V      v_mfma_f32_16x16x32 (A = P via LDS, B = V^T from LDS)
-// K is staged in LDS row-major; V is staged transposed so that each lane's
-// eight contraction values (tokens) are contiguous. Tiles are prefetched
-// kTileDepth ahead in registers through per-page buffer descriptors (an absent
-// page has no records and reads as zeros). Each workgroup writes its chunk's
-// state (o, s) as fp32; the chunks are merged by the N-state merge kernel.
+// block of 128 rows (32 per wave, two 16-row MFMA tiles) and one chunk of the
+// prefix, and runs an online softmax over the chunk in tiles of 32 tokens
+// (two pages). Everything is computed transposed, so that the softmax
+// weights never leave registers:
+//   S^T = K Q^T    v_mfma_f32_16x16x32: A = K (16 tokens x 32 d) from LDS,
+//                  B = Q^T from registers; lane (l16, grp) receives the scores
+//                  of row l16 for tokens 4grp+e and 16+4grp+e (e < 4)
+//   P^T = 2^(S^T*scale*log2e - m), rounded to the input type: those eight
+//                  weights are exactly the lane's B operand of the next product
+//                  when its contraction slot grp holds those eight tokens
+//   O^T += V^T P^T v_mfma_f32_16x16x32: A = V^T (16 d x 32 tokens) from LDS,
+//                  stored transposed with the tokens of each slot adjacent
+// The softmax denominator sums the fp32 weights, so the LSE is exact to fp32;
+// only the P V product uses the rounded weights. The running max of a row is
+// shared by the four lanes that hold it; it is raised only when a score passes
+// it by more than kRescaleSlack (rare after the first tile), which is when the
+// four lanes compare their maxima.
+//
+// LDS row strides are the ones measured free of bank conflicts on gfx950 for
+// this pattern (16 rows x 16 bytes per ds_read_b128): 288 bytes for K rows and
+// 96 bytes for V^T rows (272 and 80 bytes measured 1.7x slower, 256 bytes
+// 6.5x). The transposed V writes spread one instruction over all 16 token
+// pairs of a tile. Tiles are prefetched kDepth ahead in registers (K
+// through per-page buffer descriptors, V through per-lane global addresses); an
+// absent page contributes no tokens. Each workgroup writes its chunk's state
+// (o, s) as fp32; the chunks are merged by the N-state merge kernel.
 #include "common.h"
 #include "launch.h"
 
@@ -24,16 +39,17 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kPage = 16;
-constexpr int kBM = 64;              // query rows per workgroup
-constexpr int kBN = 32;              // prefix tokens per tile
+constexpr int kRowTiles = 2;               // 16-row MFMA tiles per wave
+constexpr int kBM = 4 * 16 * kRowTiles;    // query rows per workgroup
+constexpr int kBN = 32;                    // prefix tokens per tile
 constexpr int kThreads = 256;
-constexpr int kKStride = kD + 8;     // padded LDS row (elements) of the K tile
-constexpr int kVtStride = kBN + 8;   // padded LDS row (elements) of the transposed V tile
-constexpr int kPStride = kBN + 8;    // padded LDS row (elements) of a wave's P tile
-constexpr int kTileDepth = 3;        // tiles in flight per thread
-constexpr int kMaxChunkPages = 64;   // page ids of a chunk fit one VGPR of the wave
+constexpr int kKStride = kD + 16;          // LDS row (elements) of the K tile: 288 bytes
+constexpr int kVtStride = kBN + 16;        // LDS row (elements) of the V^T tile: 96 bytes
+constexpr int kDepth = 4;                  // tiles in flight per thread
+constexpr int kMaxChunkPages = 64;         // page ids of a chunk fit one VGPR of the wave
 constexpr int kBufferFlags = 0x00020000;
-constexpr int kTargetBlocks = 512;   // two workgroups per compute unit
+constexpr float kRescaleSlack = 8.0f;
+constexpr int kTargetBlocks = 256;        // one workgroup per compute unit
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -50,21 +66,16 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const u32x4_t& a, const u32x4_t&
                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
-// Round to the 16-bit input type (nearest even) and return the bits.
+// Two fp32 values rounded to the 16-bit input type (nearest even), packed.
 template <int DT>
-__device__ __forceinline__ uint16_t round16(float x) {
-  if constexpr (DT == MI_BF16)
-    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
-  else
-    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return DT == MI_BF16 ? pack_bf16(a, b) : pack_f16(a, b);
 }
 
-__device__ __forceinline__ float row16_max(float x) {
-  x = __builtin_fmaxf(x, dpp<kDppQuadXor1>(x));
-  x = __builtin_fmaxf(x, dpp<kDppQuadXor2>(x));
-  x = __builtin_fmaxf(x, dpp<kDppRowRor4>(x));
-  return __builtin_fmaxf(x, dpp<kDppRowRor8>(x));
-}
+// Position of tile token t in a V^T row: contraction slot g = (t % 16) / 4
+// holds tokens 4g..4g+3 then 16+4g..16+4g+3, the order in which a lane of
+// group g holds its weights.
+__device__ __forceinline__ int vt_pos(int t) { return 8 * ((t & 15) >> 2) + 4 * (t >> 4) + (t & 3); }
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void prefix_attention_kernel(
@@ -72,10 +83,8 @@ __global__ __launch_bounds__(kThreads) void prefix_attention_kernel(
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ prefix_pages, int prefix_len,
     int n_rows, int Hq, int Hkv, int G, int64_t num_phys, int chunk_tokens, int n_chunks,
     float qk_scale_log2, float* __restrict__ ws_o, float* __restrict__ ws_s) {
-  // Double-buffered K (row-major) and V (transposed) tiles; per-wave P tiles.
   __shared__ __attribute__((aligned(16))) uint16_t ks[2][kBN * kKStride];
   __shared__ __attribute__((aligned(16))) uint16_t vt[2][kD * kVtStride];
-  __shared__ __attribute__((aligned(16))) uint16_t ps[4][16 * kPStride];
 
   // Block -> (row block, kv head, chunk). The row blocks of one (kv head,
   // chunk) get ids that are equal modulo 8, so they run on one XCD and share
@@ -91,16 +100,17 @@ __global__ __launch_bounds__(kThreads) void prefix_attention_kernel(
   const int l16 = lane & 15;
   const int grp = lane >> 4;
 
-  // Q fragments (A operand): lane holds row wave*16 + l16, d = 32*k + 8*grp + [0, 8).
-  u32x4_t qa[4];
-  {
-    const int r = rb * kBM + wave * 16 + l16;
-    const int rr = r < n_rows ? r : 0;
+  // Q^T fragments (B operand): lane holds row l16 of row tile r, d = 32k + 8grp + [0, 8).
+  u32x4_t qb[kRowTiles][4];
+#pragma unroll
+  for (int r = 0; r < kRowTiles; ++r) {
+    const int row = rb * kBM + wave * (16 * kRowTiles) + 16 * r + l16;
+    const int rr = row < n_rows ? row : 0;
     const int64_t qrow = static_cast<int64_t>(rr / G) * Hq + hkv * G + (rr % G);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const u32x4_t x = *reinterpret_cast<const u32x4_t*>(q + qrow * kD + 32 * k + 8 * grp);
-      qa[k] = r < n_rows ? x : u32x4_t{0, 0, 0, 0};
+      qb[r][k] = row < n_rows ? x : u32x4_t{0, 0, 0, 0};
     }
   }
 
@@ -113,164 +123,208 @@ __global__ __launch_bounds__(kThreads) void prefix_attention_kernel(
 
   // The chunk's page ids, one per lane (a chunk spans at most 64 pages).
   const int32_t ids = (page0 + lane < n_pages) ? prefix_pages[page0 + lane] : -1;
-
-  // Tile loads: wave w takes token rows 8w .. 8w+7 of the tile, i.e. half of
-  // page w/2, so each wave's buffer descriptor is uniform. Lane l takes the
-  // token pair 8w + 2(l%4), +1 at d = 8(l/4); a load instruction covers four
-  // whole 256-byte rows, and each lane can write V^T as packed token pairs.
-  const int pr = lane & 3;
-  const int c8 = (lane >> 2) * 8;
-  const int row0 = (wave & 1) * 8 + 2 * pr;            // token row within the page
-  const int lane_bytes = (row0 * kD + c8) * 2;
-  const int64_t tile_elems = static_cast<int64_t>(kPage) * kD;
-  u32x4_t kbuf[kTileDepth][2], vbuf[kTileDepth][2];
-  auto issue = [&](int t, int j) {
-    const int pl = 2 * t + (wave >> 1);                 // page index within the chunk
-    const int32_t phys = __builtin_amdgcn_readlane(ids, pl & 63);
-    const bool ok = t < n_tiles && page0 + pl < n_pages && phys >= 0 && phys < num_phys;
-    const int64_t base = (static_cast<int64_t>(ok ? phys : 0) * Hkv + hkv) * tile_elems;
-    const int records = ok ? static_cast<int>(tile_elems * 2) : 0;
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kc + base), 0, records, kBufferFlags);
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vc + base), 0, records, kBufferFlags);
-    kbuf[j][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, lane_bytes, 0, 0));
-    kbuf[j][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, lane_bytes + kD * 2, 0, 0));
-    vbuf[j][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, lane_bytes, 0, 0));
-    vbuf[j][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, lane_bytes + kD * 2, 0, 0));
+  auto page_ok = [&](int pl, int32_t phys) {
+    return page0 + pl < n_pages && pl < 2 * n_tiles && phys >= 0 && phys < num_phys;
   };
 
-  // Stage tile t (registers slot j) into LDS buffer `buf`; tokens at or past
-  // the chunk end are zero in V (their scores are masked separately).
-  const int tk = 8 * wave + 2 * pr;                     // token pair within the tile
-  auto stage = [&](int t, int j, int buf) {
-    const int ttok = tok0 + t * kBN;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      *reinterpret_cast<u32x4_t*>(&ks[buf][(tk + h) * kKStride + c8]) = kbuf[j][h];
-    const bool v0 = ttok + tk < tok1;
-    const bool v1 = ttok + tk + 1 < tok1;
-    const u32x4_t a = v0 ? vbuf[j][0] : u32x4_t{0, 0, 0, 0};
-    const u32x4_t b = v1 ? vbuf[j][1] : u32x4_t{0, 0, 0, 0};
-    uint32_t* vtw = reinterpret_cast<uint32_t*>(vt[buf]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t x = a[i], y = b[i];
-      vtw[((c8 + 2 * i) * kVtStride + tk) / 2] = (x & 0xffffu) | (y << 16);
-      vtw[((c8 + 2 * i + 1) * kVtStride + tk) / 2] = (x >> 16) | (y & 0xffff0000u);
+  // Staging roles. K: thread (p = tid/16, c = tid%16) takes tile tokens 2p,
+  // 2p+1 at d = 8c (its wave covers one page: p/8 = wave/2). V: thread
+  // (pv = tid%16, cv = tid/16) takes tokens 2pv, 2pv+1 at d = 8cv, so that one
+  // transposed-write instruction spreads over all 16 token pairs.
+  const int kp = tid >> 4, kc8 = (tid & 15) * 8;
+  const int vp = tid & 15, vc8 = (tid >> 4) * 8;
+  const int k_lane_bytes = ((2 * (kp & 7)) * kD + kc8) * 2;
+  const int64_t tile_elems = static_cast<int64_t>(kPage) * kD;
+  u32x4_t kbuf[kDepth][2], vbuf[kDepth][2];
+  bool vok[kDepth];
+  auto issue = [&](int t, int j) {
+    {  // K: the wave's page
+      const int pl = 2 * t + (wave >> 1);
+      const int32_t phys = __builtin_amdgcn_readlane(ids, pl & 63);
+      const bool ok = page_ok(pl, phys);
+      const int64_t base = (static_cast<int64_t>(ok ? phys : 0) * Hkv + hkv) * tile_elems;
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(kc + base), 0, ok ? static_cast<int>(tile_elems * 2) : 0, kBufferFlags);
+      kbuf[j][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, k_lane_bytes, 0, 0));
+      kbuf[j][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, k_lane_bytes + kD * 2, 0, 0));
+    }
+    {  // V: the lane's page (its token pair's)
+      const int pl = 2 * t + (vp >> 3);
+      const int32_t phys0 = __builtin_amdgcn_readlane(ids, (2 * t) & 63);
+      const int32_t phys1 = __builtin_amdgcn_readlane(ids, (2 * t + 1) & 63);
+      const int32_t phys = (vp >> 3) ? phys1 : phys0;
+      const bool ok = page_ok(pl, phys);
+      vok[j] = ok;
+      const uint16_t* src = vc + (static_cast<int64_t>(ok ? phys : 0) * Hkv + hkv) * tile_elems +
+                            (2 * (vp & 7)) * kD + vc8;
+      vbuf[j][0] = *reinterpret_cast<const u32x4_t*>(src);
+      vbuf[j][1] = *reinterpret_cast<const u32x4_t*>(src + kD);
     }
   };
 
-  f32x4_t o[8];
+  // Stage tile t (register slot j) into LDS buffer `buf`: K row-major, V
+  // transposed. V of tokens at or past the chunk end or on an absent page is
+  // written as zero (its scores are masked as well).
+  auto stage = [&](int t, int j, int buf) {
+    *reinterpret_cast<u32x4_t*>(&ks[buf][(2 * kp) * kKStride + kc8]) = kbuf[j][0];
+    *reinterpret_cast<u32x4_t*>(&ks[buf][(2 * kp + 1) * kKStride + kc8]) = kbuf[j][1];
+    const int ttok = tok0 + t * kBN;
+    const bool v0 = vok[j] && ttok + 2 * vp < tok1;
+    const bool v1 = vok[j] && ttok + 2 * vp + 1 < tok1;
+    const u32x4_t a = v0 ? vbuf[j][0] : u32x4_t{0, 0, 0, 0};
+    const u32x4_t b = v1 ? vbuf[j][1] : u32x4_t{0, 0, 0, 0};
+    uint32_t* vtw = reinterpret_cast<uint32_t*>(vt[buf]);
+    const int col = vt_pos(2 * vp) >> 1;  // dword column of the token pair
 #pragma unroll
-  for (int c = 0; c < 8; ++c) o[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  float m[4], lsum[4];
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t x = a[i], y = b[i];
+      vtw[(vc8 + 2 * i) * (kVtStride / 2) + col] = (x & 0xffffu) | (y << 16);
+      vtw[(vc8 + 2 * i + 1) * (kVtStride / 2) + col] = (x >> 16) | (y & 0xffff0000u);
+    }
+  };
+
+  f32x4_t o[kRowTiles][8];
+  float m[kRowTiles], mu[kRowTiles], thr[kRowTiles], lsum[kRowTiles];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    m[e] = -kInf;
-    lsum[e] = 0.0f;
+  for (int r = 0; r < kRowTiles; ++r) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[r][c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    m[r] = -kInf;
+    mu[r] = 0.0f;
+    thr[r] = -kInf;
+    lsum[r] = 0.0f;
   }
 
   auto compute = [&](int t, int buf) {
     const int ttok = tok0 + t * kBN;
-    // S = Q K^T for the wave's 16 rows and the tile's 32 tokens (two 16-column tiles).
-    f32x4_t s[2];
+    // S^T: token tile c (tokens 16c..16c+15) x the wave's row tiles.
+    f32x4_t s[kRowTiles][2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) s[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int r = 0; r < kRowTiles; ++r)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+      for (int c = 0; c < 2; ++c) s[r][c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    // All K operands are read before the products (one wave per SIMD has no
+    // other wave to hide LDS latency behind), likewise the V^T operands below,
+    // which are read before the softmax arithmetic.
+    u32x4_t ka[4][2];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const u32x4_t kb = *reinterpret_cast<const u32x4_t*>(
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        ka[k][c] = *reinterpret_cast<const u32x4_t*>(
             &ks[buf][(16 * c + l16) * kKStride + 32 * k + 8 * grp]);
-        s[c] = mfma16x16x32<DT>(qa[k], kb, s[c]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int r = 0; r < kRowTiles; ++r) s[r][c] = mfma16x16x32<DT>(ka[k][c], qb[r][k], s[r][c]);
+    u32x4_t va[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      va[c] = *reinterpret_cast<const u32x4_t*>(&vt[buf][(16 * c + l16) * kVtStride + 8 * grp]);
+    __builtin_amdgcn_sched_barrier(0);
+    // Scores in base 2; tokens at or past the chunk end, or on an absent
+    // page, are masked.
+    bool pg[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) pg[c] = page_ok(2 * t + c, __builtin_amdgcn_readlane(ids, (2 * t + c) & 63));
+    float x[kRowTiles][8];
+    bool need = false;
+#pragma unroll
+    for (int r = 0; r < kRowTiles; ++r) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool in = pg[c] && ttok + 16 * c + 4 * grp + e < tok1;
+          x[r][4 * c + e] = in ? s[r][c][e] * qk_scale_log2 : -kInf;
+          need |= x[r][4 * c + e] > thr[r];
+        }
+    }
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      // Raise the row maxima: the four lanes of a row agree on the new max.
+#pragma unroll
+      for (int r = 0; r < kRowTiles; ++r) {
+        float mx = m[r];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mx = __builtin_fmaxf(mx, x[r][i]);
+        mx = __builtin_fmaxf(mx, shfl_xor(mx, 16));
+        mx = __builtin_fmaxf(mx, shfl_xor(mx, 32));
+        const float alpha = mx > m[r] ? __builtin_amdgcn_exp2f(m[r] - mx) : 1.0f;
+        m[r] = mx;
+        mu[r] = mx == -kInf ? 0.0f : mx;
+        thr[r] = mx + kRescaleSlack;
+        lsum[r] *= alpha;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o[r][c] *= alpha;
       }
     }
-    // Online softmax for the lane's rows 4*grp + e (columns 16c + l16).
-    uint16_t pbits[2][4];
-    float alpha[4];
-    bool moved = false;
+    // P^T as the B operand: slot grp holds tokens 4grp..4grp+3, 16+4grp..16+4grp+3.
+    u32x4_t pb[kRowTiles];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float x0 = s[0][e] * qk_scale_log2;
-      float x1 = s[1][e] * qk_scale_log2;
-      x0 = ttok + l16 < tok1 ? x0 : -kInf;
-      x1 = ttok + 16 + l16 < tok1 ? x1 : -kInf;
-      const float mn = __builtin_fmaxf(m[e], row16_max(__builtin_fmaxf(x0, x1)));
-      const float mu = mn == -kInf ? 0.0f : mn;
-      alpha[e] = __builtin_amdgcn_exp2f(m[e] - mu);
-      moved |= mn != m[e];
-      // The denominator takes the fp32 weights; only the P V product uses the
-      // weights rounded to the input type (the LSE stays exact to fp32).
-      const float p0 = __builtin_amdgcn_exp2f(x0 - mu);
-      const float p1 = __builtin_amdgcn_exp2f(x1 - mu);
-      pbits[0][e] = round16<DT>(p0);
-      pbits[1][e] = round16<DT>(p1);
-      lsum[e] = lsum[e] * alpha[e] + (p0 + p1);
-      m[e] = mn;
+    for (int r = 0; r < kRowTiles; ++r) {
+      float p[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(x[r][i] - mu[r]);
+        lsum[r] += p[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pb[r][i] = pack2<DT>(p[2 * i], p[2 * i + 1]);
     }
-    if (__builtin_amdgcn_ballot_w64(moved) != 0) {
+    // O^T += V^T P^T over the eight 16-wide d tiles.
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
+    for (int c = 0; c < 8; ++c)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) o[c][e] *= alpha[e];
-    }
-    // P to LDS (row-major per wave), read back as the A operand of P V.
-    uint16_t* pw = ps[wave];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      pw[(4 * grp + e) * kPStride + l16] = pbits[0][e];
-      pw[(4 * grp + e) * kPStride + 16 + l16] = pbits[1][e];
-    }
-    const u32x4_t pa = *reinterpret_cast<const u32x4_t*>(pw + l16 * kPStride + 8 * grp);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const u32x4_t vb = *reinterpret_cast<const u32x4_t*>(
-          &vt[buf][(16 * c + l16) * kVtStride + 8 * grp]);
-      o[c] = mfma16x16x32<DT>(pa, vb, o[c]);
-    }
+      for (int r = 0; r < kRowTiles; ++r) o[r][c] = mfma16x16x32<DT>(va[c], pb[r], o[r][c]);
   };
 
-  // Pipeline: registers hold tiles t+1 .. t+kTileDepth; tile t+1 is staged
-  // into the other LDS buffer while tile t is computed; one barrier per tile.
-  // The loop body is unconditional: tiles past the chunk end load zeros (no
-  // records) and have every score masked, so they change nothing, and the
-  // compiler can keep exact load counts across iterations.
+  // Pipeline: registers hold tiles t+1 .. t+kDepth; tile t+1 is staged into
+  // the other LDS buffer while tile t is computed; one barrier per tile. The
+  // loop body is unconditional: tiles past the chunk end load zeros (no
+  // records, or a masked page) and have every score masked, so they change
+  // nothing, and the compiler keeps exact load counts across iterations.
 #pragma unroll
-  for (int j = 0; j < kTileDepth; ++j) {
+  for (int j = 0; j < kDepth; ++j) {
     issue(j, j);
     __builtin_amdgcn_sched_barrier(0);
   }
   stage(0, 0, 0);
-  issue(kTileDepth, 0);
+  issue(kDepth, 0);
   __syncthreads();
-  const int iters = (n_tiles + kTileDepth - 1) / kTileDepth * kTileDepth;
-  for (int base = 0; base < iters; base += kTileDepth) {
+  const int iters = (n_tiles + kDepth - 1) / kDepth * kDepth;
+  for (int base = 0; base < iters; base += kDepth) {
 #pragma unroll
-    for (int j = 0; j < kTileDepth; ++j) {
+    for (int j = 0; j < kDepth; ++j) {
       const int t = base + j;
-      const int jn = (j + 1) % kTileDepth;   // register slot of tile t+1
+      const int jn = (j + 1) % kDepth;   // register slot of tile t+1
       stage(t + 1, jn, (t + 1) & 1);
-      issue(t + 1 + kTileDepth, jn);
+      issue(t + 1 + kDepth, jn);
       compute(t, t & 1);
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  // Finalise the chunk state of the lane's rows 4*grp + e, columns 16c + l16.
+  // Finalise the chunk state of row l16 of each row tile: lane (l16, grp)
+  // holds d = 16c + 4grp + e; the denominator is summed over the four lanes.
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float l = row16_sum(lsum[e]);
+  for (int r = 0; r < kRowTiles; ++r) {
+    float l = lsum[r];
+    l += shfl_xor(l, 16);
+    l += shfl_xor(l, 32);
     const float inv = guarded_inv(l);
-    const int r = rb * kBM + wave * 16 + 4 * grp + e;
-    if (r >= n_rows) continue;
-    const int64_t qrow = static_cast<int64_t>(r / G) * Hq + hkv * G + (r % G);
+    const int row = rb * kBM + wave * (16 * kRowTiles) + 16 * r + l16;
+    if (row >= n_rows) continue;
+    const int64_t qrow = static_cast<int64_t>(row / G) * Hq + hkv * G + (row % G);
     const int64_t at = qrow * n_chunks + chunk;
-    float* out = ws_o + at * kD + l16;
+    float* out = ws_o + at * kD + 4 * grp;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) out[16 * c] = o[c][e] * inv;
-    if (l16 == 0) ws_s[at] = l > 0.0f ? m[e] + hw_log2(l) : -kInf;
+    for (int c = 0; c < 8; ++c)
+      *reinterpret_cast<f32x4_t*>(out + 16 * c) = o[r][c] * inv;
+    if (grp == 0) ws_s[at] = l > 0.0f ? m[r] + hw_log2(l) : -kInf;
   }
 }
 
