@@ -5,9 +5,10 @@
 //
 // For one kv head, the query rows are the (request, query head) pairs that use
 // it: row r = req * G + g reads q[req, hkv * G + g, :]. One workgroup takes a
-// block of 128 rows (32 per wave, two 16-row MFMA tiles) and one chunk of the
+// block of 64 rows (one 16-row MFMA tile per wave) and one chunk of the
 // prefix, and runs an online softmax over the chunk in tiles of 32 tokens
-// (two pages). Everything is computed transposed, so that the softmax
+// (two pages). Two workgroups share a compute unit (two waves per SIMD), so
+// one wave's softmax arithmetic overlaps the other's matrix products. Everything is computed transposed, so that the softmax
 // weights never leave registers:
 //   S^T = K Q^T    v_mfma_f32_16x16x32: A = K (16 tokens x 32 d) from LDS,
 //                  B = Q^T from registers; lane (l16, grp) receives the scores
@@ -39,17 +40,17 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kPage = 16;
-constexpr int kRowTiles = 2;               // 16-row MFMA tiles per wave
+constexpr int kRowTiles = 1;               // 16-row MFMA tiles per wave
 constexpr int kBM = 4 * 16 * kRowTiles;    // query rows per workgroup
 constexpr int kBN = 32;                    // prefix tokens per tile
 constexpr int kThreads = 256;
 constexpr int kKStride = kD + 16;          // LDS row (elements) of the K tile: 288 bytes
 constexpr int kVtStride = kBN + 16;        // LDS row (elements) of the V^T tile: 96 bytes
-constexpr int kDepth = 4;                  // tiles in flight per thread
+constexpr int kDepth = 2;                  // tiles in flight per thread (2 measured faster than 4 or 6)
 constexpr int kMaxChunkPages = 64;         // page ids of a chunk fit one VGPR of the wave
 constexpr int kBufferFlags = 0x00020000;
 constexpr float kRescaleSlack = 8.0f;
-constexpr int kTargetBlocks = 256;        // one workgroup per compute unit
+constexpr int kTargetBlocks = 512;        // two workgroups per compute unit
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -78,7 +79,7 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 __device__ __forceinline__ int vt_pos(int t) { return 8 * ((t & 15) >> 2) + 4 * (t >> 4) + (t & 3); }
 
 template <int DT>
-__global__ __launch_bounds__(kThreads) void prefix_attention_kernel(
+__global__ __launch_bounds__(kThreads, 2) void prefix_attention_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ prefix_pages, int prefix_len,
     int n_rows, int Hq, int Hkv, int G, int64_t num_phys, int chunk_tokens, int n_chunks,
@@ -137,6 +138,7 @@ __global__ __launch_bounds__(kThreads) void prefix_attention_kernel(
   const int64_t tile_elems = static_cast<int64_t>(kPage) * kD;
   u32x4_t kbuf[kDepth][2], vbuf[kDepth][2];
   bool vok[kDepth];
+  bool vfull[kDepth];  // the whole tile is valid (uniform)
   auto issue = [&](int t, int j) {
     {  // K: the wave's page
       const int pl = 2 * t + (wave >> 1);
@@ -155,6 +157,7 @@ __global__ __launch_bounds__(kThreads) void prefix_attention_kernel(
       const int32_t phys = (vp >> 3) ? phys1 : phys0;
       const bool ok = page_ok(pl, phys);
       vok[j] = ok;
+      vfull[j] = page_ok(2 * t, phys0) && page_ok(2 * t + 1, phys1) && tok0 + (t + 1) * kBN <= tok1;
       const uint16_t* src = vc + (static_cast<int64_t>(ok ? phys : 0) * Hkv + hkv) * tile_elems +
                             (2 * (vp & 7)) * kD + vc8;
       vbuf[j][0] = *reinterpret_cast<const u32x4_t*>(src);
@@ -168,30 +171,36 @@ __global__ __launch_bounds__(kThreads) void prefix_attention_kernel(
   auto stage = [&](int t, int j, int buf) {
     *reinterpret_cast<u32x4_t*>(&ks[buf][(2 * kp) * kKStride + kc8]) = kbuf[j][0];
     *reinterpret_cast<u32x4_t*>(&ks[buf][(2 * kp + 1) * kKStride + kc8]) = kbuf[j][1];
-    const int ttok = tok0 + t * kBN;
-    const bool v0 = vok[j] && ttok + 2 * vp < tok1;
-    const bool v1 = vok[j] && ttok + 2 * vp + 1 < tok1;
-    const u32x4_t a = v0 ? vbuf[j][0] : u32x4_t{0, 0, 0, 0};
-    const u32x4_t b = v1 ? vbuf[j][1] : u32x4_t{0, 0, 0, 0};
+    u32x4_t a = vbuf[j][0], b = vbuf[j][1];
+    if (!vfull[j]) {  // the chunk's last tile, or an absent page
+      const int ttok = tok0 + t * kBN;
+      const bool v0 = vok[j] && ttok + 2 * vp < tok1;
+      const bool v1 = vok[j] && ttok + 2 * vp + 1 < tok1;
+      a = v0 ? a : u32x4_t{0, 0, 0, 0};
+      b = v1 ? b : u32x4_t{0, 0, 0, 0};
+    }
     uint32_t* vtw = reinterpret_cast<uint32_t*>(vt[buf]);
     const int col = vt_pos(2 * vp) >> 1;  // dword column of the token pair
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t x = a[i], y = b[i];
-      vtw[(vc8 + 2 * i) * (kVtStride / 2) + col] = (x & 0xffffu) | (y << 16);
-      vtw[(vc8 + 2 * i + 1) * (kVtStride / 2) + col] = (x >> 16) | (y & 0xffff0000u);
+      // Low halves of the pair's two dwords, then high halves (v_perm_b32).
+      vtw[(vc8 + 2 * i) * (kVtStride / 2) + col] = __builtin_amdgcn_perm(b[i], a[i], 0x05040100u);
+      vtw[(vc8 + 2 * i + 1) * (kVtStride / 2) + col] = __builtin_amdgcn_perm(b[i], a[i], 0x07060302u);
     }
   };
 
   f32x4_t o[kRowTiles][8];
-  float m[kRowTiles], mu[kRowTiles], thr[kRowTiles], lsum[kRowTiles];
+  // m: reference max of a row (base 2), mu: m or 0 while m = -inf (the value
+  // subtracted before exp2), gap: how far above mu a score may go before m is
+  // raised (kRescaleSlack, or -inf while m = -inf).
+  float m[kRowTiles], mu[kRowTiles], gap[kRowTiles], lsum[kRowTiles];
 #pragma unroll
   for (int r = 0; r < kRowTiles; ++r) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) o[r][c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     m[r] = -kInf;
     mu[r] = 0.0f;
-    thr[r] = -kInf;
+    gap[r] = -kInf;
     lsum[r] = 0.0f;
   }
 
@@ -225,40 +234,55 @@ __global__ __launch_bounds__(kThreads) void prefix_attention_kernel(
     for (int c = 0; c < 8; ++c)
       va[c] = *reinterpret_cast<const u32x4_t*>(&vt[buf][(16 * c + l16) * kVtStride + 8 * grp]);
     __builtin_amdgcn_sched_barrier(0);
-    // Scores in base 2; tokens at or past the chunk end, or on an absent
-    // page, are masked.
-    bool pg[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) pg[c] = page_ok(2 * t + c, __builtin_amdgcn_readlane(ids, (2 * t + c) & 63));
-    float x[kRowTiles][8];
-    bool need = false;
-#pragma unroll
-    for (int r = 0; r < kRowTiles; ++r) {
+    // y = score * scale * log2(e) - mu, one FMA per score. Tokens at or past
+    // the chunk end, or on an absent page, get y = -inf; only the chunk's last
+    // tile (or one with an absent page) needs the masks.
+    const bool full = tok0 + (t + 1) * kBN <= tok1 &&
+                      page_ok(2 * t, __builtin_amdgcn_readlane(ids, (2 * t) & 63)) &&
+                      page_ok(2 * t + 1, __builtin_amdgcn_readlane(ids, (2 * t + 1) & 63));
+    float y[kRowTiles][8];
+    auto make_y = [&](int r) {
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool in = pg[c] && ttok + 16 * c + 4 * grp + e < tok1;
-          x[r][4 * c + e] = in ? s[r][c][e] * qk_scale_log2 : -kInf;
-          need |= x[r][4 * c + e] > thr[r];
+        for (int e = 0; e < 4; ++e) y[r][4 * c + e] = __builtin_fmaf(s[r][c][e], qk_scale_log2, -mu[r]);
+      if (!full) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const bool pg = page_ok(2 * t + c, __builtin_amdgcn_readlane(ids, (2 * t + c) & 63));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool in = pg && ttok + 16 * c + 4 * grp + e < tok1;
+            y[r][4 * c + e] = in ? y[r][4 * c + e] : -kInf;
+          }
         }
+      }
+    };
+    bool need = false;
+    float ymax[kRowTiles];
+#pragma unroll
+    for (int r = 0; r < kRowTiles; ++r) {
+      make_y(r);
+      ymax[r] = y[r][0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) ymax[r] = __builtin_fmaxf(ymax[r], y[r][i]);
+      need |= ymax[r] > gap[r];
     }
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
       // Raise the row maxima: the four lanes of a row agree on the new max.
 #pragma unroll
       for (int r = 0; r < kRowTiles; ++r) {
-        float mx = m[r];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) mx = __builtin_fmaxf(mx, x[r][i]);
+        float mx = __builtin_fmaxf(m[r], ymax[r] + mu[r]);
         mx = __builtin_fmaxf(mx, shfl_xor(mx, 16));
         mx = __builtin_fmaxf(mx, shfl_xor(mx, 32));
         const float alpha = mx > m[r] ? __builtin_amdgcn_exp2f(m[r] - mx) : 1.0f;
         m[r] = mx;
         mu[r] = mx == -kInf ? 0.0f : mx;
-        thr[r] = mx + kRescaleSlack;
+        gap[r] = mx == -kInf ? -kInf : kRescaleSlack;
         lsum[r] *= alpha;
 #pragma unroll
         for (int c = 0; c < 8; ++c) o[r][c] *= alpha;
+        make_y(r);
       }
     }
     // P^T as the B operand: slot grp holds tokens 4grp..4grp+3, 16+4grp..16+4grp+3.
@@ -268,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void prefix_attention_kernel(
       float p[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(x[r][i] - mu[r]);
+        p[i] = __builtin_amdgcn_exp2f(y[r][i]);
         lsum[r] += p[i];
       }
 #pragma unroll
