@@ -13,8 +13,9 @@ Definitions followed (see the header of ``oracle.cpp`` for the full list):
 merge of two / N states, "F2 hints: merge_state, base-2 LSE merge",
 sections 3-5; LSE sanitising, "FlashAttention's empty-row LSE", section 2.2;
 softmax attention, same page, section 0; split page ranges, empty splits and
-the split-count rule, "L3 hints: split-KV decode and LSE merge", sections 2, 4
-and 6.
+the split-count rules, "L3 hints: split-KV decode and LSE merge", sections 2, 4
+and 6; the attention sink, "FlashAttention's empty-row LSE", sections 0.1 and 1;
+the masked in-place and variable-length merges, "F2 hints", section 7.
 """
 from __future__ import annotations
 
@@ -61,6 +62,12 @@ def _load():
         lib.or_plan_splits.argtypes = [I, I, P, I, I]
         lib.or_attention.argtypes = [P, I, P, P, I, P, I, P, I, I, I, I, I, D, P, P, I]
         lib.or_split_partials.argtypes = [P, I, P, P, I, P, I, P, I, I, I, I, I, D, I, P, P, I]
+        lib.or_merge_sink.argtypes = [P, P, I, I64, I, I, P, P, P, I]
+        lib.or_merge_state_masked.argtypes = [P, P, P, P, I, I64, I, I, P, P, P, I]
+        lib.or_merge_states_varlen.argtypes = [P, P, I, P, I64, I, I, P, P, I]
+        lib.or_plan_splits_varlen.argtypes = [I, I, P, I, I, P]
+        lib.or_split_partials_varlen.argtypes = [P, I, P, P, I, P, I, P, I, I, I, I, I, D, P, I,
+                                                 P, P, I]
         _lib = lib
     return _lib
 
@@ -180,4 +187,81 @@ def split_partials(q, k_cache, v_cache, page_table, ctx_lens, sm_scale: float, s
                                    _code(kv_dtype), _ptr(pt), pt.shape[1], _ptr(ctx), B, Hq, Hkv,
                                    D, page, float(sm_scale), splits, _ptr(o), _ptr(s), threads)
     _check(rc, "split_partials")
+    return o, s
+
+
+def merge_sink(v, s, sink, dtype: str, threads: int = 0):
+    """State v[S,H,D], s[S,H] merged with the sink of each head (logit sink[H],
+    natural units, value 0) -> (v fp64, s fp64)."""
+    v = np.ascontiguousarray(v)
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    sink = np.ascontiguousarray(sink, dtype=np.float32)
+    H, D = s.shape[-1], v.shape[-1]
+    assert sink.shape == (H,) and v.size == s.size * D
+    v_out = np.empty(v.shape, np.float64)
+    s_out = np.empty(s.shape, np.float64)
+    rc = _load().or_merge_sink(_ptr(v), _ptr(s), _code(dtype), s.size, H, D, _ptr(sink),
+                               _ptr(v_out), _ptr(s_out), threads)
+    _check(rc, "merge_sink")
+    return v_out, s_out
+
+
+def merge_state_masked(va, sa, vb, sb, mask, dtype: str, threads: int = 0):
+    """Two states v[S,H,D], s[S,H]; positions with mask[S] == 0 keep state a."""
+    va, vb = np.ascontiguousarray(va), np.ascontiguousarray(vb)
+    sa = np.ascontiguousarray(sa, dtype=np.float32)
+    sb = np.ascontiguousarray(sb, dtype=np.float32)
+    S, H, D = va.shape
+    m = None if mask is None else np.ascontiguousarray(mask, dtype=np.uint8)
+    assert m is None or m.shape == (S,)
+    v_out = np.empty(va.shape, np.float64)
+    s_out = np.empty(sa.shape, np.float64)
+    rc = _load().or_merge_state_masked(_ptr(va), _ptr(sa), _ptr(vb), _ptr(sb), _code(dtype), S,
+                                       H, D, None if m is None else _ptr(m), _ptr(v_out),
+                                       _ptr(s_out), threads)
+    _check(rc, "merge_state_masked")
+    return v_out, s_out
+
+
+def merge_states_varlen(v, s, indptr, dtype: str, threads: int = 0):
+    """States v[total,H,D], s[total,H]; segment i = states indptr[i]..indptr[i+1]-1
+    -> (v[S,H,D] fp64, s[S,H] fp64) with S = len(indptr) - 1."""
+    v = np.ascontiguousarray(v)
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    indptr = np.ascontiguousarray(indptr, dtype=np.int32)
+    S = indptr.size - 1
+    _, H, D = v.shape
+    v_out = np.empty((S, H, D), np.float64)
+    s_out = np.empty((S, H), np.float64)
+    rc = _load().or_merge_states_varlen(_ptr(v), _ptr(s), _code(dtype), _ptr(indptr), S, H, D,
+                                        _ptr(v_out), _ptr(s_out), threads)
+    _check(rc, "merge_states_varlen")
+    return v_out, s_out
+
+
+def plan_splits_varlen(B: int, Hkv: int, ctx_lens, page: int, num_cus: int):
+    """-> (pages per split c, split counts [B] int32)."""
+    ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+    counts = np.empty(B, np.int32)
+    c = _load().or_plan_splits_varlen(B, Hkv, _ptr(ctx), page, num_cus, _ptr(counts))
+    if c < 0:
+        raise ValueError("oracle plan_splits_varlen rejected its arguments")
+    return c, counts
+
+
+def split_partials_varlen(q, k_cache, v_cache, page_table, ctx_lens, sm_scale: float, indptr,
+                          chunk_pages: int, q_dtype: str, kv_dtype: str, threads: int = 0):
+    """Partials with per-sequence splits -> (o_part[total,Hq,D], lse_part[total,Hq]) fp64."""
+    q, k_cache, v_cache, pt, ctx, B, Hq, Hkv, D, page = _decode_common(
+        q, k_cache, v_cache, page_table, ctx_lens, q_dtype, kv_dtype)
+    indptr = np.ascontiguousarray(indptr, dtype=np.int32)
+    assert indptr.shape == (B + 1,)
+    total = int(indptr[-1])
+    o = np.empty((total, Hq, D), np.float64)
+    s = np.empty((total, Hq), np.float64)
+    rc = _load().or_split_partials_varlen(_ptr(q), _code(q_dtype), _ptr(k_cache),
+                                          _ptr(v_cache), _code(kv_dtype), _ptr(pt), pt.shape[1],
+                                          _ptr(ctx), B, Hq, Hkv, D, page, float(sm_scale),
+                                          _ptr(indptr), chunk_pages, _ptr(o), _ptr(s), threads)
+    _check(rc, "split_partials_varlen")
     return o, s

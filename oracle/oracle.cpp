@@ -20,7 +20,13 @@
 //    attention; used here for unsplit decode and for each split's partial.
 //  * "L3 hints: split-KV decode and LSE merge", section 2: page ranges of a
 //    split; section 4: an empty split writes (o = 0, lse = -inf); section 6: the
-//    rule of thumb for the number of splits.
+//    rule of thumb for the number of splits, and plan() giving sequences of
+//    different lengths different numbers of splits.
+//  * "FlashAttention's empty-row LSE", section 0.1 (table) and section 1: an
+//    attention sink rescales the output by e^L / (e^L + e^sink) and adds the
+//    sink to the LSE, i.e. it is a key of logit `sink` and value 0.
+//  * "F2 hints", section 7: merge_state_in_place (here with a per-position
+//    mask) and merge_states over many or variable-length index sets.
 //
 // Merges are written as the plain definition over the set E of non-empty states
 // (an explicit branch, not a max trick): if E is empty the result is (0, -inf);
@@ -325,6 +331,136 @@ int or_split_partials(const void* q, int q_dtype, const void* k_cache, const voi
     int t1 = std::min(p1 * page, ctx);
     if (p1 <= p0) t1 = t0;
     attend(a, b, hq, t0, t1, o_part + row * D, lse_part + row);
+  });
+  return 0;
+}
+
+// Attention sink ("FlashAttention's empty-row LSE", section 0.1 and section 1):
+// the sink of head h is a key with logit sink[h] (natural units) and value 0,
+// i.e. the state (v = 0, s = sink[h] / ln 2); the result is the merge of the
+// row's state with it. The sink is sanitised like any LSE (NaN, +inf -> no
+// sink). v [rows, D] with rows = S*H, head h = row % H; s [rows].
+int or_merge_sink(const void* v, const float* s, int v_dtype, int64_t rows, int H, int D,
+                  const float* sink, double* v_out, double* s_out, int threads) {
+  if (!v || !s || !sink || !v_out || !s_out || rows < 0 || H <= 0 || D <= 0 || !dtype_ok(v_dtype))
+    return 1;
+  parallel_rows(rows, threads, [&](int64_t r) {
+    const double sk = static_cast<double>(sink[r % H]) / std::log(2.0);
+    double sv[2] = {sanitize(s[r]), sanitize(sk)};
+    std::vector<double> vv(2 * static_cast<size_t>(D), 0.0);
+    for (int d = 0; d < D; ++d) vv[d] = load_elem(v, v_dtype, r * D + d);
+    merge_definition(2, sv, vv.data(), D, v_out + r * D, s_out + r);
+  });
+  return 0;
+}
+
+// Two states with a per-position mask (merge_state_in_place's optional mask,
+// "F2 hints", section 7; its meaning is a reading, see the design notes):
+// positions whose mask byte is 0 keep state a unchanged (not even sanitised);
+// the others get merge(a, b). v [S,H,D], s [S,H], mask [S] (NULL: all merge).
+int or_merge_state_masked(const void* va, const float* sa, const void* vb, const float* sb,
+                          int v_dtype, int64_t S, int H, int D, const uint8_t* mask,
+                          double* v_out, double* s_out, int threads) {
+  if (!va || !sa || !vb || !sb || !v_out || !s_out || S < 0 || H <= 0 || D <= 0 ||
+      !dtype_ok(v_dtype))
+    return 1;
+  parallel_rows(S * H, threads, [&](int64_t r) {
+    if (mask != nullptr && mask[r / H] == 0) {
+      for (int d = 0; d < D; ++d) v_out[r * D + d] = load_elem(va, v_dtype, r * D + d);
+      s_out[r] = static_cast<double>(sa[r]);
+      return;
+    }
+    double sv[2] = {sanitize(sa[r]), sanitize(sb[r])};
+    std::vector<double> vv(2 * static_cast<size_t>(D));
+    for (int d = 0; d < D; ++d) {
+      vv[d] = load_elem(va, v_dtype, r * D + d);
+      vv[D + d] = load_elem(vb, v_dtype, r * D + d);
+    }
+    merge_definition(2, sv, vv.data(), D, v_out + r * D, s_out + r);
+  });
+  return 0;
+}
+
+// Variable-length merge ("F2 hints", section 4 formula over index sets of any
+// size): states v [total, H, D], s [total, H]; segment i (i < S) is the states
+// indptr[i] .. indptr[i+1]-1 and merges into v_out [S, H, D], s_out [S, H]. An
+// empty segment is the empty state.
+int or_merge_states_varlen(const void* v, const float* s, int v_dtype, const int32_t* indptr,
+                           int64_t S, int H, int D, double* v_out, double* s_out, int threads) {
+  if (!v || !s || !indptr || !v_out || !s_out || S < 0 || H <= 0 || D <= 0 || !dtype_ok(v_dtype))
+    return 1;
+  for (int64_t i = 0; i < S; ++i)
+    if (indptr[i] < 0 || indptr[i + 1] < indptr[i]) return 1;
+  parallel_rows(S * H, threads, [&](int64_t row) {
+    const int64_t seg = row / H;
+    const int h = static_cast<int>(row % H);
+    const int n = indptr[seg + 1] - indptr[seg];
+    std::vector<double> sv(n > 0 ? n : 1);
+    std::vector<double> vv(static_cast<size_t>(n > 0 ? n : 1) * D);
+    for (int k = 0; k < n; ++k) {
+      const int64_t idx = static_cast<int64_t>(indptr[seg] + k) * H + h;
+      sv[k] = sanitize(s[idx]);
+      for (int d = 0; d < D; ++d) vv[static_cast<size_t>(k) * D + d] = load_elem(v, v_dtype, idx * D + d);
+    }
+    merge_definition(n, sv.data(), vv.data(), D, v_out + row * D, s_out + row);
+  });
+  return 0;
+}
+
+// Per-sequence split counts ("L3 hints", section 6: plan() may give sequences
+// of different lengths different numbers of splits). Reading: every split of
+// every sequence covers the same number of pages c, the smallest c >= 8 for
+// which the work items Hkv * sum_b max(1, ceil(np_b / c)) are at most twice the
+// CU count (c stops growing at the longest sequence's page count); sequence b
+// gets max(1, ceil(np_b / c)) splits. Returns c, or -1 on bad arguments; the
+// counts go to counts[B]. Found by counting up from 8.
+int or_plan_splits_varlen(int B, int Hkv, const int32_t* ctx_lens, int page, int num_cus,
+                          int32_t* counts) {
+  if (B <= 0 || Hkv <= 0 || !ctx_lens || page <= 0 || num_cus <= 0 || !counts) return -1;
+  std::vector<int64_t> np(B);
+  int64_t max_np = 0;
+  for (int b = 0; b < B; ++b) {
+    if (ctx_lens[b] < 0) return -1;
+    np[b] = ctx_lens[b] / page + (ctx_lens[b] % page != 0 ? 1 : 0);
+    max_np = std::max(max_np, np[b]);
+  }
+  auto items = [&](int64_t c) {
+    int64_t w = 0;
+    for (int b = 0; b < B; ++b) w += std::max<int64_t>(1, np[b] / c + (np[b] % c != 0 ? 1 : 0));
+    return w * Hkv;
+  };
+  int64_t c = 8;
+  while (c < max_np && items(c) > 2LL * num_cus) ++c;
+  for (int b = 0; b < B; ++b)
+    counts[b] = static_cast<int32_t>(std::max<int64_t>(1, np[b] / c + (np[b] % c != 0 ? 1 : 0)));
+  return static_cast<int>(c);
+}
+
+// Partials with per-sequence splits: split k of sequence b (global index
+// indptr[b] + k) covers pages [k*c, min((k+1)*c, np_b)), i.e. tokens
+// [k*c*page, min((k+1)*c*page, ctx)). o_part [total, Hq, D], lse_part
+// [total, Hq] (base 2); a split without tokens is (0, -inf).
+int or_split_partials_varlen(const void* q, int q_dtype, const void* k_cache, const void* v_cache,
+                             int kv_dtype, const int32_t* page_table, int pt_stride,
+                             const int32_t* ctx_lens, int B, int Hq, int Hkv, int D, int page,
+                             double sm_scale, const int32_t* indptr, int chunk_pages,
+                             double* o_part, double* lse_part, int threads) {
+  DecodeArgs a{q, q_dtype, k_cache, v_cache, kv_dtype, page_table, pt_stride, ctx_lens,
+               B, Hq, Hkv, D, page, sm_scale};
+  if (!decode_args_ok(a) || !indptr || chunk_pages <= 0 || !o_part || !lse_part) return 1;
+  const int total = indptr[B];
+  std::vector<int> owner(total > 0 ? total : 1);
+  for (int b = 0; b < B; ++b)
+    for (int i = indptr[b]; i < indptr[b + 1]; ++i) owner[i] = b;
+  parallel_rows(static_cast<int64_t>(total) * Hq, threads, [&](int64_t row) {
+    const int i = static_cast<int>(row / Hq);
+    const int hq = static_cast<int>(row % Hq);
+    const int b = owner[i];
+    const int k = i - indptr[b];
+    const int64_t t0 = static_cast<int64_t>(k) * chunk_pages * page;
+    const int64_t t1 = std::min<int64_t>(t0 + static_cast<int64_t>(chunk_pages) * page, ctx_lens[b]);
+    attend(a, b, hq, static_cast<int>(t0), static_cast<int>(t1 > t0 ? t1 : t0), o_part + row * D,
+           lse_part + row);
   });
   return 0;
 }
