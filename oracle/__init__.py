@@ -66,8 +66,8 @@ def _load():
         lib.or_merge_state_masked.argtypes = [P, P, P, P, I, I64, I, I, P, P, P, I]
         lib.or_merge_states_varlen.argtypes = [P, P, I, P, I64, I, I, P, P, I]
         lib.or_plan_splits_varlen.argtypes = [I, I, P, I, I, P]
-        lib.or_split_partials_varlen.argtypes = [P, I, P, P, I, P, I, P, I, I, I, I, I, D, P, I,
-                                                 P, P, I]
+        lib.or_split_partials_varlen.argtypes = [P, I, P, P, I, P, I, P, I, I, I, I, I, D, P, P,
+                                                 P, I]
         _lib = lib
     return _lib
 
@@ -250,8 +250,9 @@ def plan_splits_varlen(B: int, Hkv: int, ctx_lens, page: int, num_cus: int):
 
 
 def split_partials_varlen(q, k_cache, v_cache, page_table, ctx_lens, sm_scale: float, indptr,
-                          chunk_pages: int, q_dtype: str, kv_dtype: str, threads: int = 0):
-    """Partials with per-sequence splits -> (o_part[total,Hq,D], lse_part[total,Hq]) fp64."""
+                          q_dtype: str, kv_dtype: str, threads: int = 0):
+    """Partials with per-sequence splits (sequence b has indptr[b+1] - indptr[b] >= 1 splits,
+    each with the page-range formula) -> (o_part[total,Hq,D], lse_part[total,Hq]) fp64."""
     q, k_cache, v_cache, pt, ctx, B, Hq, Hkv, D, page = _decode_common(
         q, k_cache, v_cache, page_table, ctx_lens, q_dtype, kv_dtype)
     indptr = np.ascontiguousarray(indptr, dtype=np.int32)
@@ -262,6 +263,6 @@ def split_partials_varlen(q, k_cache, v_cache, page_table, ctx_lens, sm_scale: f
     rc = _load().or_split_partials_varlen(_ptr(q), _code(q_dtype), _ptr(k_cache),
                                           _ptr(v_cache), _code(kv_dtype), _ptr(pt), pt.shape[1],
                                           _ptr(ctx), B, Hq, Hkv, D, page, float(sm_scale),
-                                          _ptr(indptr), chunk_pages, _ptr(o), _ptr(s), threads)
+                                          _ptr(indptr), _ptr(o), _ptr(s), threads)
     _check(rc, "split_partials_varlen")
     return o, s

@@ -408,12 +408,14 @@ int or_merge_states_varlen(const void* v, const float* s, int v_dtype, const int
 }
 
 // Per-sequence split counts ("L3 hints", section 6: plan() may give sequences
-// of different lengths different numbers of splits). Reading: every split of
-// every sequence covers the same number of pages c, the smallest c >= 8 for
-// which the work items Hkv * sum_b max(1, ceil(np_b / c)) are at most twice the
-// CU count (c stops growing at the longest sequence's page count); sequence b
-// gets max(1, ceil(np_b / c)) splits. Returns c, or -1 on bad arguments; the
-// counts go to counts[B]. Found by counting up from 8.
+// of different lengths different numbers of splits). Reading: the uniform rule
+// carried over to one page budget c shared by all sequences. The work items
+// Hkv * sum_b max(1, ceil(np_b / c)) should reach twice the CU count with as
+// few items as possible, so c is the largest value (up to the longest
+// sequence's page count) whose items still reach it; a split keeps at least 8
+// pages, so c never goes below 8. Sequence b gets max(1, ceil(np_b / c))
+// splits. Returns c, or -1 on bad arguments; the counts go to counts[B].
+// Found by counting down from the longest page count.
 int or_plan_splits_varlen(int B, int Hkv, const int32_t* ctx_lens, int page, int num_cus,
                           int32_t* counts) {
   if (B <= 0 || Hkv <= 0 || !ctx_lens || page <= 0 || num_cus <= 0 || !counts) return -1;
@@ -429,38 +431,41 @@ int or_plan_splits_varlen(int B, int Hkv, const int32_t* ctx_lens, int page, int
     for (int b = 0; b < B; ++b) w += std::max<int64_t>(1, np[b] / c + (np[b] % c != 0 ? 1 : 0));
     return w * Hkv;
   };
-  int64_t c = 8;
-  while (c < max_np && items(c) > 2LL * num_cus) ++c;
+  int64_t c = max_np;
+  while (c > 8 && items(c) < 2LL * num_cus) --c;
+  if (c < 8) c = 8;
   for (int b = 0; b < B; ++b)
     counts[b] = static_cast<int32_t>(std::max<int64_t>(1, np[b] / c + (np[b] % c != 0 ? 1 : 0)));
   return static_cast<int>(c);
 }
 
-// Partials with per-sequence splits: split k of sequence b (global index
-// indptr[b] + k) covers pages [k*c, min((k+1)*c, np_b)), i.e. tokens
-// [k*c*page, min((k+1)*c*page, ctx)). o_part [total, Hq, D], lse_part
-// [total, Hq] (base 2); a split without tokens is (0, -inf).
+// Partials with per-sequence splits: sequence b has n_b = indptr[b+1] -
+// indptr[b] splits, and its split k (global index indptr[b] + k) takes the
+// page range of the section-2 formula with n_b splits. o_part [total, Hq, D],
+// lse_part [total, Hq] (base 2); a split without tokens is (0, -inf).
 int or_split_partials_varlen(const void* q, int q_dtype, const void* k_cache, const void* v_cache,
                              int kv_dtype, const int32_t* page_table, int pt_stride,
                              const int32_t* ctx_lens, int B, int Hq, int Hkv, int D, int page,
-                             double sm_scale, const int32_t* indptr, int chunk_pages,
-                             double* o_part, double* lse_part, int threads) {
+                             double sm_scale, const int32_t* indptr, double* o_part,
+                             double* lse_part, int threads) {
   DecodeArgs a{q, q_dtype, k_cache, v_cache, kv_dtype, page_table, pt_stride, ctx_lens,
                B, Hq, Hkv, D, page, sm_scale};
-  if (!decode_args_ok(a) || !indptr || chunk_pages <= 0 || !o_part || !lse_part) return 1;
+  if (!decode_args_ok(a) || !indptr || !o_part || !lse_part || indptr[0] != 0) return 1;
+  for (int b = 0; b < B; ++b)
+    if (indptr[b + 1] <= indptr[b]) return 1;
   const int total = indptr[B];
-  std::vector<int> owner(total > 0 ? total : 1);
+  std::vector<int> owner(total);
   for (int b = 0; b < B; ++b)
     for (int i = indptr[b]; i < indptr[b + 1]; ++i) owner[i] = b;
   parallel_rows(static_cast<int64_t>(total) * Hq, threads, [&](int64_t row) {
     const int i = static_cast<int>(row / Hq);
     const int hq = static_cast<int>(row % Hq);
     const int b = owner[i];
-    const int k = i - indptr[b];
-    const int64_t t0 = static_cast<int64_t>(k) * chunk_pages * page;
-    const int64_t t1 = std::min<int64_t>(t0 + static_cast<int64_t>(chunk_pages) * page, ctx_lens[b]);
-    attend(a, b, hq, static_cast<int>(t0), static_cast<int>(t1 > t0 ? t1 : t0), o_part + row * D,
-           lse_part + row);
+    int p0, p1;
+    split_pages(ctx_lens[b], page, indptr[b + 1] - indptr[b], i - indptr[b], &p0, &p1);
+    const int t0 = p0 * page;
+    const int t1 = std::min(p1 * page, ctx_lens[b]);
+    attend(a, b, hq, t0, t1 > t0 ? t1 : t0, o_part + row * D, lse_part + row);
   });
   return 0;
 }

@@ -144,6 +144,8 @@ def _items(nps, c, Hkv):
 
 @pytest.mark.parametrize("seed", range(12))
 def test_varlen_plan_meets_its_defining_conditions(seed):
+    # c: the largest pages-per-split (at most the longest sequence, at least 8)
+    # whose work items still reach twice the CU count.
     g = np.random.default_rng(seed)
     B = int(g.integers(1, 65))
     Hkv = int(g.choice([1, 2, 8]))
@@ -152,22 +154,37 @@ def test_varlen_plan_meets_its_defining_conditions(seed):
     c, counts = oracle.plan_splits_varlen(B, Hkv, ctx, 16, cus)
     nps = _np(ctx, 16)
     cap = 2 * cus
-    assert c >= 8
-    assert _items(nps, c, Hkv) <= cap or c >= max(nps)
-    if c > 8:
-        assert _items(nps, c - 1, Hkv) > cap          # nothing smaller qualifies
+    if max(nps) <= 8:
+        assert c == 8
+    else:
+        assert 8 <= c <= max(nps)
+        assert c == 8 or _items(nps, c, Hkv) >= cap
+        assert c == max(nps) or _items(nps, c + 1, Hkv) < cap   # nothing larger qualifies
     assert list(counts) == [max(1, -(-n // c)) for n in nps]
 
 
 def test_varlen_plan_examples():
+    # "L3 hints", section 6 table, first row: one 32K sequence, Hkv = 8 -> the
+    # uniform plan's 64 splits of 32 pages.
     c, counts = oracle.plan_splits_varlen(1, 8, np.array([32768]), 16, 256)
-    assert (c, list(counts)) == (32, [64])            # the uniform plan's 64 splits
+    assert (c, list(counts)) == (32, [64])
     c, counts = oracle.plan_splits_varlen(2, 8, np.array([32768, 100]), 16, 256)
-    assert counts[1] == 1 and counts[0] >= 30         # the short sequence is not split
+    assert (c, list(counts)) == (33, [63, 1])         # the short sequence is not split
     c, counts = oracle.plan_splits_varlen(4, 8, np.array([0, 0, 0, 0]), 16, 256)
     assert c == 8 and list(counts) == [1, 1, 1, 1]
+    # third row: B*Hkv = 512 already twice the CUs -> no split.
     c, counts = oracle.plan_splits_varlen(64, 8, np.full(64, 1024), 16, 256)
-    assert c == 64 and set(counts) == {1}             # B*Hkv already twice the CUs
+    assert c == 64 and set(counts) == {1}
+    # second row (8 x 4096, 170 CUs as on the page's GPU): 16 splits of 16 pages
+    # reach 1024 >= 340 items; the largest such c gives ceil(256/c) = 6 splits.
+    c, counts = oracle.plan_splits_varlen(8, 8, np.full(8, 4096), 16, 170)
+    assert (c, set(counts)) == (51, {6})
+    # equal lengths reduce to the largest c that the uniform rule's target allows
+    for B, n in ((1, 2048), (8, 256), (3, 1000)):
+        c, counts = oracle.plan_splits_varlen(B, 8, np.full(B, n * 16), 16, 256)
+        k = -(-n // c)
+        assert B * 8 * k >= 512 or c == 8
+        assert B * 8 * -(-n // (c + 1)) < 512 or c == n
 
 
 # ----------------------------------------------------------------------------- per-sequence partials
@@ -176,15 +193,16 @@ def test_varlen_partials_zero_query_closed_form():
     ctx = np.array([37, 1000, 1, 0, 300], np.int32)
     case = inputs.paged_kv_case(12, ctx, 4, 2, 16, 16, dtype="f16")
     case["q"][:] = 0
-    c, counts = oracle.plan_splits_varlen(5, 2, ctx, 16, 4)
+    counts = np.array([4, 7, 2, 3, 1], np.int32)
     indptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     o, s = oracle.split_partials_varlen(case["q"], case["k"], case["v"], case["page_table"], ctx,
-                                        case["sm_scale"], indptr, c, "f16", "f16")
+                                        case["sm_scale"], indptr, "f16", "f16")
     vdec = oracle.decode_f16(case["v"])
     for b, n in enumerate(ctx):
         covered = 0
         for k in range(counts[b]):
-            t0, t1 = k * c * 16, min((k + 1) * c * 16, int(n))
+            p0, p1 = oracle.split_range(int(n), 16, int(counts[b]), k)   # pinned page ranges
+            t0, t1 = p0 * 16, min(p1 * 16, int(n))
             i = indptr[b] + k
             if t1 <= t0:
                 assert np.all(s[i] == -np.inf) and not o[i].any()
@@ -198,14 +216,25 @@ def test_varlen_partials_zero_query_closed_form():
         assert covered == n
 
 
+def test_varlen_partials_with_uniform_counts_are_the_uniform_partials():
+    ctx = np.array([37, 1000, 1, 300], np.int32)
+    case = inputs.paged_kv_case(14, ctx, 4, 2, 16, 16, dtype="bf16")
+    args = (case["q"], case["k"], case["v"], case["page_table"], ctx, case["sm_scale"])
+    ou, su = oracle.split_partials(*args, 4, "bf16", "bf16")         # [B, Hq, 4, D]
+    indptr = np.arange(0, 17, 4, dtype=np.int32)
+    ov, sv = oracle.split_partials_varlen(*args, indptr, "bf16", "bf16")
+    assert np.array_equal(ov.reshape(4, 4, 4, 16).transpose(0, 2, 1, 3), ou)
+    assert np.array_equal(sv.reshape(4, 4, 4).transpose(0, 2, 1), su)
+
+
 def test_varlen_partials_merge_to_unsplit_attention():
     ctx = inputs.mixed_ctx_lens(13, 12, hi=3000)
     case = inputs.paged_kv_case(13, ctx, 8, 2, 32, 16, dtype="bf16")
     args = (case["q"], case["k"], case["v"], case["page_table"], ctx, case["sm_scale"])
     c, counts = oracle.plan_splits_varlen(12, 2, ctx, 16, 64)
     indptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
-    assert counts.max() > 1
-    op, sp = oracle.split_partials_varlen(*args, indptr, c, "bf16", "bf16")
+    assert counts.max() > 1 and counts.min() == 1
+    op, sp = oracle.split_partials_varlen(*args, indptr, "bf16", "bf16")
     mo, ms = oracle.merge_states_varlen(op.astype(np.float32), sp.astype(np.float32), indptr, "f32")
     o, s = oracle.attention(*args, "bf16", "bf16")
     assert np.allclose(mo, o, rtol=1e-5, atol=1e-6)
