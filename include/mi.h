@@ -87,6 +87,60 @@ mi_status mi_merge_states(const void* v, const float* s, void* v_out, float* s_o
                           void* stream);
 
 /*
+ * Two-state merge in place with an optional per-position mask (the
+ * merge_state_in_place variant named in "F2 hints: merge_state, base-2 LSE
+ * merge", section 7; section 3 for the merge itself).
+ *   v, s       : [S, H, D] of v_dtype and [S, H] fp32 base 2, read and updated
+ *   v_other,
+ *   s_other    : [S, H, D] of v_dtype and [S, H] fp32, read only
+ *   mask       : [S] bytes (device, may be NULL = merge every position);
+ *                positions whose byte is 0 are left exactly as they were
+ *                (their s is not even sanitised); the others get
+ *                merge((v, s), (v_other, s_other)).
+ * No overlap between v/s and the other arguments. S == 0 is a no-op. D must be
+ * a positive multiple of 8, at most 512.
+ */
+mi_status mi_merge_state_in_place(void* v, float* s, const void* v_other, const float* s_other,
+                                  const uint8_t* mask, int64_t S, int32_t H, int32_t D,
+                                  mi_dtype v_dtype, void* stream);
+
+/*
+ * Fold an attention sink into each state ("FlashAttention's empty-row LSE",
+ * table of section 0 and the FlashMLA branch of section 2.1): the sink acts
+ * as one extra key of logit sink[h] whose value is 0, i.e. a merge with the
+ * state (v = 0, s = sink[h] * log2 e). v is scaled by 2^s / (2^s + 2^sink2)
+ * and s becomes log2(2^s + 2^sink2), sink2 = sink * log2 e.
+ *   v, s    : [S, H, D] of v_dtype, [S, H] fp32 base 2
+ *   sink    : [H] fp32 (device), natural-log logits, one per head; -inf means
+ *             no sink, and NaN / +inf count as -inf like any LSE
+ *   v_out   : [S, H, D] of out_dtype; s_out : [S, H] fp32 (may be NULL)
+ * An empty state becomes (0, sink2). In-place use is allowed (v_out == v when
+ * out_dtype == v_dtype, s_out == s); any other overlap is MI_ERR_ALIAS.
+ * S == 0 is a no-op. D must be a positive multiple of 8, at most 512.
+ */
+mi_status mi_merge_sink(const void* v, const float* s, const float* sink, void* v_out,
+                        float* s_out, int64_t S, int32_t H, int32_t D, mi_dtype v_dtype,
+                        mi_dtype out_dtype, void* stream);
+
+/*
+ * Merge index sets of any size ("F2 hints", section 4's N-state merge over
+ * variable-length sets; section 7's many-index-set variant).
+ *   v      : [total, H, D] of v_dtype      s : [total, H] fp32 base 2
+ *   indptr : [S + 1] int32 (device); set p is the states indptr[p] ..
+ *            indptr[p+1] - 1 (entries are clamped to [0, total]; an empty set
+ *            gives (0, -inf))
+ *   v_out  : [S, H, D] of out_dtype        s_out : [S, H] fp32 (may be NULL)
+ * Each (p, h) is served by one or more whole waves, so a set of thousands of
+ * states is merged without a second launch. With indptr[p] = p * N it is
+ * mi_merge_states on [S, N, H, D]. Used with fp32 v and H = Hq it is the
+ * combine of per-sequence split decode. Outputs must not overlap inputs.
+ * S == 0 is a no-op. D must be a positive multiple of 8, at most 512.
+ */
+mi_status mi_merge_states_varlen(const void* v, const float* s, const int32_t* indptr,
+                                 int64_t total, void* v_out, float* s_out, int64_t S, int32_t H,
+                                 int32_t D, mi_dtype v_dtype, mi_dtype out_dtype, void* stream);
+
+/*
  * Choose the number of KV splits for one decode step ("L3 hints: split-KV
  * decode and LSE merge", section 6: make B*Hkv*splits a few times the compute
  * unit count while each split keeps several pages; do not split when B*Hkv is
@@ -172,6 +226,52 @@ mi_status mi_split_kv_decode_fused(const void* q, const void* k_cache, const voi
                                    int32_t num_splits, float sm_scale, mi_dtype kv_dtype,
                                    float* o_part, float* lse_part, int32_t* counters, void* o,
                                    float* lse, mi_dtype out_dtype, void* stream);
+
+/*
+ * Per-sequence split counts for one decode step ("L3 hints: split-KV decode
+ * and LSE merge", section 6: plan() can give sequences of different lengths
+ * different numbers of splits). Host only; ctx_lens_host is a HOST array.
+ * Rule (the uniform rule carried over to one page budget c per split): c is
+ * the largest value in [8, longest sequence's page count] for which the work
+ * items Hkv * sum_b max(1, ceil(pages_b / c)) still reach 2 * num_cus (8 if
+ * none does); sequence b gets max(1, ceil(pages_b / c)) splits. Writes the
+ * running sums to split_indptr_host[0 .. B] (split_indptr_host[0] = 0; the
+ * last entry is the total). num_cus <= 0 asks the current HIP device.
+ */
+mi_status mi_plan_splits_varlen(int32_t B, int32_t Hkv, const int32_t* ctx_lens_host,
+                                int32_t page_size, int32_t num_cus, int32_t* split_indptr_host);
+
+/*
+ * Split-KV paged decode with per-sequence split counts ("L3 hints", sections
+ * 1-6). Sequence b is cut into n_b = split_indptr[b+1] - split_indptr[b]
+ * splits, split k taking the page range of mi_split_range with n_b splits; one
+ * workgroup per (kv head, split) over all sequences' splits.
+ *   split_indptr : [B + 1] int32 (device), as written by mi_plan_splits_varlen:
+ *                  split_indptr[0] = 0, n_b >= 1, last entry = total_splits
+ *   o_part       : [total_splits, Hq, D] fp32   lse_part : [total_splits, Hq] fp32
+ *                  caller-owned workspaces, left holding the partials (row
+ *                  split_indptr[b] + k is split k of sequence b)
+ *   counters     : [B, Hkv] int32 device workspace, or NULL. NULL: two
+ *                  launches (pass 1, then mi_merge_states_varlen as the
+ *                  combine). Given: one launch whose last workgroup per
+ *                  (sequence, kv head) merges the splits; the counters must be
+ *                  all zero before the first call and every call leaves them
+ *                  zero; calls sharing them must not run concurrently.
+ *   o            : [B, Hq, D] of out_dtype;  lse : [B, Hq] fp32 base 2 (may be NULL)
+ * Other arguments, layouts, clamping of device data and supported sizes as in
+ * mi_split_kv_partial; additionally B <= 4031 and total_splits <= 65535.
+ * A sequence given no split (equal consecutive split_indptr entries) is
+ * written (0, -inf) by the two-launch path and left unwritten by the
+ * single-launch path.
+ */
+mi_status mi_split_kv_decode_varlen(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* page_table, int32_t pt_stride,
+                                    const int32_t* ctx_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                                    int32_t D, int32_t page_size, int64_t num_phys_pages,
+                                    const int32_t* split_indptr, int32_t total_splits,
+                                    float sm_scale, mi_dtype kv_dtype, float* o_part,
+                                    float* lse_part, int32_t* counters, void* o, float* lse,
+                                    mi_dtype out_dtype, void* stream);
 
 /*
  * Cascade level 0 ("F2 hints: merge_state, base-2 LSE merge", section 6): R

@@ -43,6 +43,14 @@ SIGNATURES = {
     "mi_prefix_attention": [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I64, _F,
                             ctypes.c_int, _P, ctypes.c_size_t, _P, _P, ctypes.c_int, _P],
     "mi_prefix_attention_workspace": [_I32, _I32, _I32, _I32, _I32, _P],
+    "mi_merge_state_in_place": [_P, _P, _P, _P, _P, _I64, _I32, _I32, ctypes.c_int, _P],
+    "mi_merge_sink": [_P, _P, _P, _P, _P, _I64, _I32, _I32, ctypes.c_int, ctypes.c_int, _P],
+    "mi_merge_states_varlen": [_P, _P, _P, _I64, _P, _P, _I64, _I32, _I32, ctypes.c_int,
+                               ctypes.c_int, _P],
+    "mi_plan_splits_varlen": [_I32, _I32, _P, _I32, _I32, _P],
+    "mi_split_kv_decode_varlen": [_P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I64,
+                                  _P, _I32, _F, ctypes.c_int, _P, _P, _P, _P, _P, ctypes.c_int,
+                                  _P],
 }
 
 
@@ -146,6 +154,65 @@ def merge_states(v, s, out_dtype=None, v_out=None, s_out=None, return_s=True):
     return v_out, s_out
 
 
+def merge_state_in_place(v, s, v_other, s_other, mask=None):
+    """v, s <- merge((v, s), (v_other, s_other)) where mask [S] (bool / uint8) is set;
+    positions with a zero mask byte are left untouched. v [S, H, D] or [S, D]."""
+    _check_cuda(v, s, v_other, s_other, mask)
+    _f32(s, "s"), _f32(s_other, "s_other")
+    if v.shape != v_other.shape or s.shape != s_other.shape or v.shape[:-1] != s.shape:
+        raise ValueError("merge_state_in_place: v [S, (H,) D] and s [S, (H)] for both states")
+    if v.dtype != v_other.dtype:
+        raise TypeError("merge_state_in_place: v and v_other must share one dtype")
+    S = s.shape[0] if s.dim() > 0 else 1
+    H = s.numel() // S if S > 0 else 1
+    D = v.shape[-1]
+    if mask is not None:
+        if mask.dtype == torch.bool:
+            mask = mask.view(torch.uint8)
+        if mask.dtype != torch.uint8 or mask.shape != (S,):
+            raise ValueError("mask must be bool or uint8 of shape [S]")
+    _call("mi_merge_state_in_place", _ptr(v), _ptr(s), _ptr(v_other), _ptr(s_other), _ptr(mask),
+          S, max(H, 1), D, _dt(v), _stream(v))
+    return v, s
+
+
+def merge_sink(v, s, sink, out_dtype=None, v_out=None, s_out=None, return_s=True):
+    """Fold an attention sink (natural-log logit per head, sink [H] float32) into
+    states v [S, H, D], s [S, H] -> (v, s). v_out / s_out may be v / s."""
+    _check_cuda(v, s, sink, v_out, s_out)
+    _f32(s, "s"), _f32(sink, "sink"), _f32(s_out, "s_out")
+    if v.dim() != 3 or s.shape != v.shape[:2] or sink.shape != (v.shape[1],):
+        raise ValueError("merge_sink: v [S, H, D], s [S, H], sink [H]")
+    S, H, D = v.shape
+    out_dtype = out_dtype or (v_out.dtype if v_out is not None else v.dtype)
+    if v_out is None:
+        v_out = torch.empty(v.shape, dtype=out_dtype, device=v.device)
+    if s_out is None and return_s:
+        s_out = torch.empty(s.shape, dtype=torch.float32, device=v.device)
+    _call("mi_merge_sink", _ptr(v), _ptr(s), _ptr(sink), _ptr(v_out), _ptr(s_out), S, H, D,
+          _dt(v), _dt(v_out), _stream(v))
+    return v_out, s_out
+
+
+def merge_states_varlen(v, s, indptr, out_dtype=None, v_out=None, s_out=None, return_s=True):
+    """Merge variable-length index sets: v [total, H, D], s [total, H], indptr [S+1]
+    int32 (device) -> (v [S, H, D], s [S, H])."""
+    _check_cuda(v, s, indptr, v_out, s_out)
+    _f32(s, "s"), _f32(s_out, "s_out")
+    if v.dim() != 3 or s.shape != v.shape[:2] or indptr.dim() != 1 or indptr.dtype != torch.int32:
+        raise ValueError("merge_states_varlen: v [total, H, D], s [total, H], indptr int32 [S+1]")
+    total, H, D = v.shape
+    S = indptr.shape[0] - 1
+    out_dtype = out_dtype or (v_out.dtype if v_out is not None else v.dtype)
+    if v_out is None:
+        v_out = torch.empty((S, H, D), dtype=out_dtype, device=v.device)
+    if s_out is None and return_s:
+        s_out = torch.empty((S, H), dtype=torch.float32, device=v.device)
+    _call("mi_merge_states_varlen", _ptr(v), _ptr(s), _ptr(indptr), total, _ptr(v_out),
+          _ptr(s_out), S, H, D, _dt(v), _dt(v_out), _stream(v))
+    return v_out, s_out
+
+
 # ----------------------------------------------------------------------------- planning
 
 def plan_splits(ctx_lens, Hkv: int, page_size: int = 16, num_cus: int = 0) -> int:
@@ -157,6 +224,17 @@ def plan_splits(ctx_lens, Hkv: int, page_size: int = 16, num_cus: int = 0) -> in
     _call("mi_plan_splits", len(ctx), Hkv, ctx.ctypes.data_as(ctypes.c_void_p), page_size,
           num_cus, ctypes.byref(out))
     return out.value
+
+
+def plan_splits_varlen(ctx_lens, Hkv: int, page_size: int = 16, num_cus: int = 0):
+    """Per-sequence split counts -> split_indptr (numpy int32 [B+1], host)."""
+    import numpy as np
+    ctx = np.ascontiguousarray(np.asarray(ctx_lens.cpu() if isinstance(ctx_lens, torch.Tensor)
+                                          else ctx_lens, dtype=np.int32))
+    out = np.empty(len(ctx) + 1, np.int32)
+    _call("mi_plan_splits_varlen", len(ctx), Hkv, ctx.ctypes.data_as(ctypes.c_void_p), page_size,
+          num_cus, out.ctypes.data_as(ctypes.c_void_p))
+    return out
 
 
 def split_range(ctx: int, page_size: int, num_splits: int, split: int):
@@ -247,6 +325,49 @@ def split_kv_decode_fused(q, k_cache, v_cache, page_table, ctx_lens, num_splits:
     _check_cuda(o_part, lse_part, out, lse, counters)
     _call("mi_split_kv_decode_fused", _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
           page_table.shape[1], _ptr(ctx_lens), B, Hq, Hkv, D, page, P, num_splits,
+          float(sm_scale), _dt(q), _ptr(o_part), _ptr(lse_part), _ptr(counters), _ptr(out),
+          _ptr(lse), _dt(out), _stream(q))
+    if return_partials:
+        return out, lse, o_part, lse_part
+    return out, lse
+
+
+def split_kv_decode_varlen(q, k_cache, v_cache, page_table, ctx_lens, split_indptr,
+                           sm_scale: float, fused: bool = True, counters=None, out_dtype=None,
+                           o_part=None, lse_part=None, out=None, lse=None, return_lse=True,
+                           return_partials=False):
+    """Decode with per-sequence split counts. ``split_indptr`` is int32 [B+1] on the
+    device (from ``plan_splits_varlen``); its last entry (the total) is read from the
+    host copy when given as numpy, else fetched once. -> (o, lse[, o_part [total, Hq, D],
+    lse_part [total, Hq]])."""
+    import numpy as np
+    B, Hq, Hkv, D, page, P = _decode_args(q, k_cache, v_cache, page_table, ctx_lens)
+    if isinstance(split_indptr, np.ndarray):
+        total = int(split_indptr[-1])
+        split_indptr = torch.from_numpy(np.ascontiguousarray(split_indptr, np.int32)).to(q.device)
+    else:
+        total = int(split_indptr[-1].item())
+    _check_cuda(split_indptr)
+    if split_indptr.dtype != torch.int32 or split_indptr.shape != (B + 1,):
+        raise ValueError("split_indptr must be int32 [B + 1]")
+    out_dtype = out_dtype or (out.dtype if out is not None else q.dtype)
+    if fused and counters is None:
+        counters = torch.zeros((B, Hkv), dtype=torch.int32, device=q.device)
+    if not fused:
+        counters = None
+    if counters is not None and (counters.dtype != torch.int32 or counters.numel() < B * Hkv):
+        raise ValueError("counters must be int32 with at least B * Hkv entries")
+    if o_part is None:
+        o_part = torch.empty((total, Hq, D), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((total, Hq), dtype=torch.float32, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check_cuda(o_part, lse_part, out, lse, counters)
+    _call("mi_split_kv_decode_varlen", _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+          page_table.shape[1], _ptr(ctx_lens), B, Hq, Hkv, D, page, P, _ptr(split_indptr), total,
           float(sm_scale), _dt(q), _ptr(o_part), _ptr(lse_part), _ptr(counters), _ptr(out),
           _ptr(lse), _dt(out), _stream(q))
     if return_partials:

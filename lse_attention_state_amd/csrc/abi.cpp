@@ -2,6 +2,7 @@
 // the caller's stream. Nothing is allocated, freed or synchronised here.
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cstdint>
 
 #include "launch.h"
@@ -9,6 +10,11 @@
 #include "split_range.h"
 
 namespace {
+
+// Per-sequence split decode: sequences (the device-side segment search reads
+// at most 64 entries per round, two rounds) and work items (grid height).
+constexpr int32_t kMaxVarlenSeqs = 4031;
+constexpr int32_t kMaxVarlenSplits = 65535;
 
 bool dtype_ok(int dt) { return dt == MI_F16 || dt == MI_BF16 || dt == MI_F32; }
 
@@ -55,11 +61,14 @@ struct DecodeShape {
   int64_t q_bytes, cache_bytes, pt_bytes, ctx_bytes, opart_bytes, lpart_bytes;
 };
 
+// part_rows: partial states per query head (B * num_splits for the uniform
+// layout; 0 means that, otherwise the per-sequence layout's total splits).
 mi_status check_decode(const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* page_table, int32_t pt_stride, const int32_t* ctx_lens,
                        int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size,
                        int64_t num_phys_pages, int32_t num_splits, mi_dtype kv_dtype,
-                       const float* o_part, const float* lse_part, DecodeShape* shp) {
+                       const float* o_part, const float* lse_part, DecodeShape* shp,
+                       int64_t part_rows = 0) {
   if (!q || !k_cache || !v_cache || !page_table || !ctx_lens || !o_part || !lse_part)
     return MI_ERR_NULL;
   if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || page_size <= 0 || pt_stride <= 0 ||
@@ -81,8 +90,10 @@ mi_status check_decode(const void* q, const void* k_cache, const void* v_cache,
   shp->cache_bytes = num_phys_pages * Hkv * page_size * D * 2;
   shp->pt_bytes = int64_t(B) * pt_stride * 4;
   shp->ctx_bytes = int64_t(B) * 4;
-  shp->opart_bytes = int64_t(B) * Hq * num_splits * D * 4;
-  shp->lpart_bytes = int64_t(B) * Hq * num_splits * 4;
+  if (part_rows == 0) part_rows = int64_t(B) * num_splits;
+  if (!size_ok(part_rows, Hq, D * 4)) return MI_ERR_SHAPE;
+  shp->opart_bytes = part_rows * Hq * D * 4;
+  shp->lpart_bytes = part_rows * Hq * 4;
   const void* ins[5] = {q, k_cache, v_cache, page_table, ctx_lens};
   const int64_t in_bytes[5] = {shp->q_bytes, shp->cache_bytes, shp->cache_bytes, shp->pt_bytes,
                                shp->ctx_bytes};
@@ -309,6 +320,173 @@ mi_status mi_split_kv_decode_fused(const void* q, const void* k_cache, const voi
                                               sm_scale, kv_dtype, o_part, lse_part,
                                               static_cast<hipStream_t>(stream), counters, o, lse,
                                               out_dtype));
+}
+
+mi_status mi_merge_state_in_place(void* v, float* s, const void* v_other, const float* s_other,
+                                  const uint8_t* mask, int64_t S, int32_t H, int32_t D,
+                                  mi_dtype v_dtype, void* stream) {
+  if (!v || !s || !v_other || !s_other) return MI_ERR_NULL;
+  if (S < 0) return MI_ERR_SHAPE;
+  mi_status st = check_merge_dims(H, D, v_dtype, v_dtype);
+  if (st != MI_OK) return st;
+  if (!size_ok(S, H, D, 4)) return MI_ERR_SHAPE;
+  if (!aligned(v, 16) || !aligned(v_other, 16) || !aligned(s, 4) || !aligned(s_other, 4))
+    return MI_ERR_UNSUPPORTED;
+  const int64_t rows = S * H;
+  const int64_t vb = rows * D * dtype_bytes(v_dtype);
+  const int64_t sb = rows * 4;
+  if (overlaps(v, vb, v_other, vb) || overlaps(v, vb, s_other, sb) || overlaps(v, vb, mask, S) ||
+      overlaps(v, vb, s, sb) || overlaps(s, sb, v_other, vb) || overlaps(s, sb, s_other, sb) ||
+      overlaps(s, sb, mask, S))
+    return MI_ERR_ALIAS;
+  if (rows == 0) return MI_OK;
+  return from_hip(mi::launch_merge_state_masked(v, s, v_other, s_other, mask, rows, H, D, v_dtype,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+mi_status mi_merge_sink(const void* v, const float* s, const float* sink, void* v_out,
+                        float* s_out, int64_t S, int32_t H, int32_t D, mi_dtype v_dtype,
+                        mi_dtype out_dtype, void* stream) {
+  if (!v || !s || !sink || !v_out) return MI_ERR_NULL;
+  if (S < 0) return MI_ERR_SHAPE;
+  mi_status st = check_merge_dims(H, D, v_dtype, out_dtype);
+  if (st != MI_OK) return st;
+  if (!size_ok(S, H, D, 4)) return MI_ERR_SHAPE;
+  if (!aligned(v, 16) || !aligned(v_out, 16) || !aligned(s, 4) || !aligned(s_out, 4) ||
+      !aligned(sink, 4))
+    return MI_ERR_UNSUPPORTED;
+  const int64_t rows = S * H;
+  const int64_t in_b = rows * D * dtype_bytes(v_dtype);
+  const int64_t out_b = rows * D * dtype_bytes(out_dtype);
+  const int64_t sb = rows * 4;
+  const int64_t kb = int64_t(H) * 4;
+  if (bad_alias(v_out, out_b, v, in_b, v_dtype == out_dtype) || overlaps(v_out, out_b, s, sb) ||
+      overlaps(v_out, out_b, sink, kb) || bad_alias(s_out, sb, s, sb, true) ||
+      overlaps(s_out, sb, v, in_b) || overlaps(s_out, sb, sink, kb) ||
+      overlaps(s_out, sb, v_out, out_b))
+    return MI_ERR_ALIAS;
+  if (rows == 0) return MI_OK;
+  return from_hip(mi::launch_merge_sink(v, s, sink, v_out, s_out, rows, H, D, v_dtype, out_dtype,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+mi_status mi_merge_states_varlen(const void* v, const float* s, const int32_t* indptr,
+                                 int64_t total, void* v_out, float* s_out, int64_t S, int32_t H,
+                                 int32_t D, mi_dtype v_dtype, mi_dtype out_dtype, void* stream) {
+  if (!v || !s || !indptr || !v_out) return MI_ERR_NULL;
+  if (S < 0 || total < 0 || total > INT32_MAX) return MI_ERR_SHAPE;
+  mi_status st = check_merge_dims(H, D, v_dtype, out_dtype);
+  if (st != MI_OK) return st;
+  if (!size_ok(total, H, D, 4) || !size_ok(S, H, D, 4)) return MI_ERR_SHAPE;
+  if (!aligned(v, 16) || !aligned(v_out, 16) || !aligned(s, 4) || !aligned(s_out, 4) ||
+      !aligned(indptr, 4))
+    return MI_ERR_UNSUPPORTED;
+  const int64_t in_v = total * H * D * dtype_bytes(v_dtype);
+  const int64_t in_s = total * H * 4;
+  const int64_t ip = (S + 1) * 4;
+  const int64_t out_v = S * H * D * dtype_bytes(out_dtype);
+  const int64_t out_s = S * H * 4;
+  if (overlaps(v_out, out_v, v, in_v) || overlaps(v_out, out_v, s, in_s) ||
+      overlaps(v_out, out_v, indptr, ip) || overlaps(s_out, out_s, v, in_v) ||
+      overlaps(s_out, out_s, s, in_s) || overlaps(s_out, out_s, indptr, ip) ||
+      overlaps(s_out, out_s, v_out, out_v))
+    return MI_ERR_ALIAS;
+  if (S == 0) return MI_OK;
+  return from_hip(mi::launch_merge_segments(v, s, indptr, total, 0, v_out, s_out, S, H, D, v_dtype,
+                                            out_dtype, static_cast<hipStream_t>(stream)));
+}
+
+mi_status mi_plan_splits_varlen(int32_t B, int32_t Hkv, const int32_t* ctx_lens_host,
+                                int32_t page_size, int32_t num_cus, int32_t* split_indptr_host) {
+  if (!ctx_lens_host || !split_indptr_host) return MI_ERR_NULL;
+  if (B <= 0 || Hkv <= 0 || page_size <= 0) return MI_ERR_SHAPE;
+  int64_t max_np = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    if (ctx_lens_host[b] < 0) return MI_ERR_SHAPE;
+    const int64_t np = (int64_t(ctx_lens_host[b]) + page_size - 1) / page_size;
+    if (np > max_np) max_np = np;
+  }
+  if (num_cus <= 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        num_cus <= 0)
+      return MI_ERR_HIP;
+  }
+  // Work items when every split holds at most c pages; never increases with c.
+  auto items = [&](int64_t c) {
+    int64_t w = 0;
+    for (int32_t b = 0; b < B; ++b) {
+      const int64_t np = (int64_t(ctx_lens_host[b]) + page_size - 1) / page_size;
+      w += np > c ? (np + c - 1) / c : 1;
+    }
+    return w * Hkv;
+  };
+  // "L3 hints", section 6, per sequence: the largest page budget c whose work
+  // items still reach twice the compute units (the fewest items that fill the
+  // device), but at least 8 pages per split. Bisection over [8, max_np].
+  const int64_t target = 2 * int64_t(num_cus);
+  int64_t c = 8;
+  if (max_np > 8 && items(8) >= target) {
+    int64_t lo = 8, hi = max_np;  // items(lo) >= target holds throughout
+    while (lo < hi) {
+      const int64_t mid = lo + (hi - lo + 1) / 2;
+      if (items(mid) >= target)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    c = lo;
+  }
+  int64_t acc = 0;
+  split_indptr_host[0] = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t np = (int64_t(ctx_lens_host[b]) + page_size - 1) / page_size;
+    acc += np > c ? (np + c - 1) / c : 1;
+    if (acc > INT32_MAX) return MI_ERR_SHAPE;
+    split_indptr_host[b + 1] = static_cast<int32_t>(acc);
+  }
+  return MI_OK;
+}
+
+mi_status mi_split_kv_decode_varlen(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* page_table, int32_t pt_stride,
+                                    const int32_t* ctx_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                                    int32_t D, int32_t page_size, int64_t num_phys_pages,
+                                    const int32_t* split_indptr, int32_t total_splits,
+                                    float sm_scale, mi_dtype kv_dtype, float* o_part,
+                                    float* lse_part, int32_t* counters, void* o, float* lse,
+                                    mi_dtype out_dtype, void* stream) {
+  if (!o || !split_indptr) return MI_ERR_NULL;
+  if (B < 0 || total_splits < 0 || (B > 0 && total_splits < B)) return MI_ERR_SHAPE;
+  if (B > kMaxVarlenSeqs || total_splits > kMaxVarlenSplits) return MI_ERR_UNSUPPORTED;
+  DecodeShape shp;
+  mi_status st = check_decode(q, k_cache, v_cache, page_table, pt_stride, ctx_lens, B, Hq, Hkv, D,
+                              page_size, num_phys_pages, 1, kv_dtype, o_part, lse_part, &shp,
+                              total_splits > 0 ? total_splits : 1);
+  if (st != MI_OK) return st;
+  st = check_decode_outputs(q, k_cache, v_cache, page_table, ctx_lens, o_part, lse_part, counters,
+                            counters != nullptr, o, lse, B, Hq, Hkv, D, out_dtype, shp);
+  if (st != MI_OK) return st;
+  if (!aligned(split_indptr, 4)) return MI_ERR_UNSUPPORTED;
+  const int64_t ip_b = (int64_t(B) + 1) * 4;
+  const int64_t o_b = int64_t(B) * Hq * D * dtype_bytes(out_dtype);
+  if (overlaps(split_indptr, ip_b, o_part, shp.opart_bytes) ||
+      overlaps(split_indptr, ip_b, lse_part, shp.lpart_bytes) ||
+      overlaps(split_indptr, ip_b, o, o_b) || overlaps(split_indptr, ip_b, lse, int64_t(B) * Hq * 4) ||
+      overlaps(split_indptr, ip_b, counters, counters ? int64_t(B) * Hkv * 4 : 0))
+    return MI_ERR_ALIAS;
+  if (B == 0) return MI_OK;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = mi::launch_split_kv_partial_varlen(
+      q, k_cache, v_cache, page_table, pt_stride, ctx_lens, B, Hq, Hkv, num_phys_pages,
+      split_indptr, total_splits, sm_scale, kv_dtype, o_part, lse_part, hs, counters, o, lse,
+      out_dtype);
+  if (e != hipSuccess || counters != nullptr) return from_hip(e);
+  // The combine: o_part [total, Hq, D] holds sequence b's splits at rows
+  // split_indptr[b] .. split_indptr[b+1]-1 -- a segmented merge with H = Hq.
+  return from_hip(mi::launch_merge_segments(o_part, lse_part, split_indptr, total_splits, 0, o, lse,
+                                            B, Hq, D, MI_F32, out_dtype, hs));
 }
 
 mi_status mi_prefix_attention_workspace(int32_t R, int32_t Hq, int32_t Hkv, int32_t D,

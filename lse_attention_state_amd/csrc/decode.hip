@@ -88,34 +88,36 @@ __device__ __forceinline__ void unpack8(const u32x4_t& w, float (&x)[8]) {
 }
 
 // The combine of one (sequence, query head) row by one wave: merge the
-// num_splits partial states o_part[row, :, :], lse_part[row, :] ("L3 hints:
-// split-KV decode and LSE merge", section 3) into o[row, :] (dtype DTO) and
-// lse[row] (base 2, optional). Lane l owns the 8-element chunk (l%16)*8 of D
-// for the splits k = l/16 (mod 4); each pass keeps 8 of its splits' loads in
-// flight, then the four split sub-groups are merged across lanes.
+// `count` partial states of that row ("L3 hints: split-KV decode and LSE
+// merge", section 3) into o[row, :] (dtype DTO) and lse[row] (base 2,
+// optional). Split j's state is lse_part[first + j * stride] and
+// o_part[(first + j * stride) * D, ...]: stride 1 for the uniform layout
+// [B, Hq, splits], Hq for the per-sequence layout [total, Hq]. Lane l owns the
+// 8-element chunk (l%16)*8 of D for the splits j = l/16 (mod 4); each pass
+// keeps 8 of its splits' loads in flight, then the four split sub-groups are
+// merged across lanes.
 template <int DTO>
-__device__ void combine_row(const float* o_part, const float* lse_part, int64_t row,
-                            int num_splits, void* o, float* lse, int lane) {
+__device__ void combine_row(const float* o_part, const float* lse_part, int64_t first,
+                            int64_t stride, int count, int64_t row, void* o, float* lse,
+                            int lane) {
   const int c = lane & 15;
   const int sg = lane >> 4;
-  const float* lp = lse_part + row * num_splits;
-  const float* op = o_part + row * num_splits * kD + c * 8;
   float m = -kInf, z = 0.0f, acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-  for (int k0 = sg; k0 < num_splits; k0 += 32) {
+  for (int k0 = sg; k0 < count; k0 += 32) {
     float sv[8], x[8][8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int k = k0 + 4 * u;
-      const int kk = k < num_splits ? k : 0;
-      sv[u] = lp[kk];
-      load8<MI_F32>(op, static_cast<int64_t>(kk) * kD, x[u]);
+      const int64_t r = first + static_cast<int64_t>(k < count ? k : 0) * stride;
+      sv[u] = lse_part[r];
+      load8<MI_F32>(o_part, r * kD + c * 8, x[u]);
     }
     float cm = m;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      sv[u] = k0 + 4 * u < num_splits ? sanitize_lse(sv[u]) : -kInf;
+      sv[u] = k0 + 4 * u < count ? sanitize_lse(sv[u]) : -kInf;
       cm = __builtin_fmaxf(cm, sv[u]);
     }
     const float keep = guarded_exp2(m - cm);
@@ -153,23 +155,81 @@ __device__ void combine_row(const float* o_part, const float* lse_part, int64_t 
   }
 }
 
+// Per-sequence splits: the sequence b that owns work item `item`, i.e. the b
+// with indptr[b] <= item < indptr[b+1], and that range. Two rounds of a 64-way
+// search by the whole wave: lane j first reads indptr at j * stride
+// (stride = ceil((B+1)/64) <= 63), the ballot of entries <= item brackets b to
+// one stride, and a second read of that bracket finds it. Empty segments are
+// skipped by construction (the last entry <= item wins). Results are clamped
+// to valid ranges whatever the device data holds: b in [0, B), and
+// 0 <= first <= end <= total.
+__device__ __forceinline__ void find_segment(const int32_t* indptr, int B, int item, int total,
+                                             int* b_out, int* first, int* end) {
+  const int lane = __lane_id();
+  const int stride = (B + 64) / 64;
+  auto probe = [&](int base, int step, int* jl, int* val) {
+    int j = base + lane * step;
+    j = j < B ? j : B;
+    *val = indptr[j];
+    const uint64_t below = __builtin_amdgcn_ballot_w64(*val <= item);
+    const int cnt = __builtin_popcountll(below);
+    *jl = cnt > 0 ? cnt - 1 : 0;
+  };
+  int jl, val;
+  probe(0, stride, &jl, &val);
+  int base = 0;
+  if (stride > 1) {
+    base = jl * stride;
+    probe(base, 1, &jl, &val);
+  }
+  int b = base + jl;
+  int lo = __builtin_amdgcn_readlane(val, jl);
+  int hi = __builtin_amdgcn_readlane(val, jl < 63 ? jl + 1 : 63);
+  b = b < B ? b : B - 1;
+  lo = lo < 0 ? 0 : (lo > total ? total : lo);
+  hi = hi < lo ? lo : (hi > total ? total : hi);
+  *b_out = b;
+  *first = lo;
+  *end = hi;
+}
+
 // DTO < 0: pass 1 only. DTO = an output dtype: pass 1 fused with the combine
 // (the last workgroup of each (sequence, kv head) to finish merges the splits).
-template <int DT, int G, int DTO>
+// kVar: per-sequence split counts. blockIdx.y is then a work item of the
+// index pointer array split_indptr [B+1] (sequence b owns items
+// split_indptr[b] .. split_indptr[b+1]-1, item k of it being split k of that
+// many), and the partials are laid out [total items, Hq, D] / [total, Hq].
+// Otherwise blockIdx.y is the split and blockIdx.z the sequence, and the
+// partials are [B, Hq, num_splits, D] / [B, Hq, num_splits].
+template <int DT, int G, int DTO, bool kVar>
 __global__ __launch_bounds__(kThreads) void split_kv_partial_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ page_table, int pt_stride,
     const int32_t* __restrict__ ctx_lens, int Hkv, int64_t num_phys, int num_splits,
     float qk_scale_log2, float* __restrict__ o_part, float* __restrict__ lse_part,
-    int32_t* __restrict__ counters, void* __restrict__ o, float* __restrict__ lse) {
+    int32_t* __restrict__ counters, void* __restrict__ o, float* __restrict__ lse,
+    const int32_t* __restrict__ split_indptr, int B) {
   __shared__ float lds_acc[kWaves][G][kD];
   __shared__ float lds_ml[kWaves][G][2];
 
   // blockIdx.x is the kv head: consecutive workgroups go round-robin to the
   // XCDs, so each kv head's splits stay on one XCD (and its L2).
   const int hkv = blockIdx.x;
-  const int split = blockIdx.y;
-  const int b = blockIdx.z;
+  int b, split, nsplit;  // sequence, split within it, its number of splits
+  int seg_first = 0;     // kVar: the sequence's first work item
+  if constexpr (kVar) {
+    const int item = blockIdx.y;
+    int seg_end;
+    find_segment(split_indptr, B, item, static_cast<int>(gridDim.y), &b, &seg_first, &seg_end);
+    b = __builtin_amdgcn_readfirstlane(b);
+    seg_first = __builtin_amdgcn_readfirstlane(seg_first);
+    nsplit = __builtin_amdgcn_readfirstlane(seg_end - seg_first);
+    split = item - seg_first;
+  } else {
+    split = blockIdx.y;
+    b = blockIdx.z;
+    nsplit = num_splits;
+  }
   // The wave index is uniform across the wave: readfirstlane tells the
   // compiler so (it keeps wave-derived values in scalar registers).
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -185,8 +245,10 @@ __global__ __launch_bounds__(kThreads) void split_kv_partial_kernel(
   ctx64 = ctx64 < 0 ? 0 : ctx64;
   const int64_t cap = static_cast<int64_t>(pt_stride) * kPage;
   const int ctx = static_cast<int>(ctx64 < cap ? ctx64 : cap);
-  int p0, p1;
-  split_pages(ctx, kPage, num_splits, split, &p0, &p1);
+  int p0 = 0, p1 = 0;
+  // (kVar with inconsistent device data: an item outside its sequence's range
+  // attends to nothing.)
+  if (split >= 0 && split < nsplit) split_pages(ctx, kPage, nsplit, split, &p0, &p1);
   const int npages = p1 > p0 ? p1 - p0 : 0;
 
   u32x4_t qw[G];
@@ -382,14 +444,17 @@ __global__ __launch_bounds__(kThreads) void split_kv_partial_kernel(
     }
     const float inv = guarded_inv(Z);
     const int64_t row = static_cast<int64_t>(b) * Hq + hkv * G + h;
-    float* out = o_part + (row * num_splits + split) * kD + 2 * lane;
+    // This split's partial row: [B, Hq, splits] or [total, Hq].
+    const int64_t prow = kVar ? static_cast<int64_t>(blockIdx.y) * Hq + hkv * G + h
+                              : row * num_splits + split;
+    float* out = o_part + prow * kD + 2 * lane;
     const float2 res = make_float2(o0 * inv, o1 * inv);
     const float lse_val = (Z > 0.0f) ? M + hw_log2(Z) : -kInf;
     if constexpr (DTO >= 0) {
-      if (num_splits == 1) {
+      if (nsplit == 1) {
         // One split: the combine is the identity, so write the result directly.
         *reinterpret_cast<float2*>(out) = res;
-        if (lane == 0) lse_part[row] = lse_val;
+        if (lane == 0) lse_part[prow] = lse_val;
         if constexpr (DTO == MI_F32) {
           *reinterpret_cast<float2*>(static_cast<float*>(o) + row * kD + 2 * lane) = res;
         } else {
@@ -404,16 +469,15 @@ __global__ __launch_bounds__(kThreads) void split_kv_partial_kernel(
       __hip_atomic_store(reinterpret_cast<uint64_t*>(out), __builtin_bit_cast(uint64_t, res),
                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (lane == 0)
-        __hip_atomic_store(lse_part + row * num_splits + split, lse_val, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(lse_part + prow, lse_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
       *reinterpret_cast<float2*>(out) = res;
-      if (lane == 0) lse_part[row * num_splits + split] = lse_val;
+      if (lane == 0) lse_part[prow] = lse_val;
     }
   }
 
   if constexpr (DTO >= 0) {
-    if (num_splits == 1) return;  // written directly above
+    if (nsplit == 1) return;  // written directly above
     // Hand-off: every workgroup publishes its partials (agent-scope release)
     // and bumps the (sequence, kv head) counter; the one that brings it to
     // num_splits performs the acquire and merges all splits of its heads.
@@ -426,32 +490,38 @@ __global__ __launch_bounds__(kThreads) void split_kv_partial_kernel(
     if (threadIdx.x == 0) {
       const int prev = __hip_atomic_fetch_add(counters + static_cast<int64_t>(b) * Hkv + hkv, 1,
                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      is_last = prev == num_splits - 1;
+      is_last = prev == nsplit - 1;
     }
     __syncthreads();
     if (!is_last) return;
     // Acquire at agent scope: drop stale lines before reading other
     // workgroups' partials.
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    for (int h = wave; h < G; h += kWaves)
-      combine_row<DTO>(o_part, lse_part, static_cast<int64_t>(b) * Hq + hkv * G + h, num_splits,
-                       o, lse, lane);
+    for (int h = wave; h < G; h += kWaves) {
+      const int64_t row = static_cast<int64_t>(b) * Hq + hkv * G + h;
+      if constexpr (kVar)
+        combine_row<DTO>(o_part, lse_part, static_cast<int64_t>(seg_first) * Hq + hkv * G + h, Hq,
+                         nsplit, row, o, lse, lane);
+      else
+        combine_row<DTO>(o_part, lse_part, row * num_splits, 1, nsplit, row, o, lse, lane);
+    }
     if (threadIdx.x == 0) counters[static_cast<int64_t>(b) * Hkv + hkv] = 0;
   }
 }
 
-template <int DT, int DTO>
+template <int DT, int DTO, bool kVar>
 hipError_t launch_group(int G, dim3 grid, hipStream_t st, const void* q, const void* kc,
                         const void* vc, const int32_t* pt, int pt_stride, const int32_t* ctx,
                         int Hkv, int64_t num_phys, int num_splits, float scale, float* o_part,
-                        float* lse_part, int32_t* counters, void* o, float* lse) {
+                        float* lse_part, int32_t* counters, void* o, float* lse,
+                        const int32_t* split_indptr, int B) {
   const uint16_t* q16 = static_cast<const uint16_t*>(q);
   const uint16_t* k16 = static_cast<const uint16_t*>(kc);
   const uint16_t* v16 = static_cast<const uint16_t*>(vc);
 #define MI_LAUNCH_G(GG)                                                                        \
-  split_kv_partial_kernel<DT, GG, DTO><<<grid, kThreads, 0, st>>>(                             \
+  split_kv_partial_kernel<DT, GG, DTO, kVar><<<grid, kThreads, 0, st>>>(                       \
       q16, k16, v16, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part, \
-      counters, o, lse)
+      counters, o, lse, split_indptr, B)
   switch (G) {
     case 1: MI_LAUNCH_G(1); break;
     case 2: MI_LAUNCH_G(2); break;
@@ -462,20 +532,21 @@ hipError_t launch_group(int G, dim3 grid, hipStream_t st, const void* q, const v
   return hipGetLastError();
 }
 
-template <int DT>
+template <int DT, bool kVar>
 hipError_t launch_dtype(int out_dtype, int G, dim3 grid, hipStream_t st, const void* q,
                         const void* kc, const void* vc, const int32_t* pt, int pt_stride,
                         const int32_t* ctx, int Hkv, int64_t num_phys, int num_splits, float scale,
-                        float* o_part, float* lse_part, int32_t* counters, void* o, float* lse) {
+                        float* o_part, float* lse_part, int32_t* counters, void* o, float* lse,
+                        const int32_t* split_indptr, int B) {
   switch (out_dtype) {
     case MI_F16:
-      return launch_group<DT, MI_F16>(G, grid, st, q, kc, vc, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part, counters, o, lse);
+      return launch_group<DT, MI_F16, kVar>(G, grid, st, q, kc, vc, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part, counters, o, lse, split_indptr, B);
     case MI_BF16:
-      return launch_group<DT, MI_BF16>(G, grid, st, q, kc, vc, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part, counters, o, lse);
+      return launch_group<DT, MI_BF16, kVar>(G, grid, st, q, kc, vc, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part, counters, o, lse, split_indptr, B);
     case MI_F32:
-      return launch_group<DT, MI_F32>(G, grid, st, q, kc, vc, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part, counters, o, lse);
+      return launch_group<DT, MI_F32, kVar>(G, grid, st, q, kc, vc, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part, counters, o, lse, split_indptr, B);
     default:
-      return launch_group<DT, -1>(G, grid, st, q, kc, vc, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part, nullptr, nullptr, nullptr);
+      return launch_group<DT, -1, kVar>(G, grid, st, q, kc, vc, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part, nullptr, nullptr, nullptr, split_indptr, B);
   }
 }
 
@@ -496,12 +567,32 @@ hipError_t launch_split_kv_partial(const void* q, const void* kc, const void* vc
   // single split (no combine needed); otherwise pass 1 only.
   const int dto = (counters != nullptr || (o != nullptr && num_splits == 1)) ? out_dtype : -1;
   if (kv_dtype == MI_F16)
-    return launch_dtype<MI_F16>(dto, G, grid, st, q, kc, vc, page_table, pt_stride, ctx_lens, Hkv,
-                                num_phys_pages, num_splits, scale, o_part, lse_part, counters, o,
-                                lse);
-  return launch_dtype<MI_BF16>(dto, G, grid, st, q, kc, vc, page_table, pt_stride, ctx_lens, Hkv,
-                               num_phys_pages, num_splits, scale, o_part, lse_part, counters, o,
-                               lse);
+    return launch_dtype<MI_F16, false>(dto, G, grid, st, q, kc, vc, page_table, pt_stride,
+                                       ctx_lens, Hkv, num_phys_pages, num_splits, scale, o_part,
+                                       lse_part, counters, o, lse, nullptr, B);
+  return launch_dtype<MI_BF16, false>(dto, G, grid, st, q, kc, vc, page_table, pt_stride,
+                                      ctx_lens, Hkv, num_phys_pages, num_splits, scale, o_part,
+                                      lse_part, counters, o, lse, nullptr, B);
+}
+
+hipError_t launch_split_kv_partial_varlen(const void* q, const void* kc, const void* vc,
+                                          const int32_t* page_table, int pt_stride,
+                                          const int32_t* ctx_lens, int B, int Hq, int Hkv,
+                                          int64_t num_phys_pages, const int32_t* split_indptr,
+                                          int total_splits, float sm_scale, int kv_dtype,
+                                          float* o_part, float* lse_part, hipStream_t st,
+                                          int32_t* counters, void* o, float* lse, int out_dtype) {
+  const int G = Hq / Hkv;
+  const dim3 grid(static_cast<unsigned>(Hkv), static_cast<unsigned>(total_splits), 1);
+  const float scale = static_cast<float>(static_cast<double>(sm_scale) * 1.4426950408889634);
+  const int dto = counters != nullptr ? out_dtype : -1;
+  if (kv_dtype == MI_F16)
+    return launch_dtype<MI_F16, true>(dto, G, grid, st, q, kc, vc, page_table, pt_stride,
+                                      ctx_lens, Hkv, num_phys_pages, 0, scale, o_part, lse_part,
+                                      counters, o, lse, split_indptr, B);
+  return launch_dtype<MI_BF16, true>(dto, G, grid, st, q, kc, vc, page_table, pt_stride,
+                                     ctx_lens, Hkv, num_phys_pages, 0, scale, o_part, lse_part,
+                                     counters, o, lse, split_indptr, B);
 }
 
 }  // namespace mi

@@ -13,6 +13,20 @@ hipError_t launch_merge_state(const void* va, const float* sa, const void* vb, c
 hipError_t launch_merge_states(const void* v, const float* s, void* vo, float* so, int64_t S,
                                int N, int H, int D, int dt_in, int dt_out, hipStream_t stream);
 
+// In place: rows of positions whose mask byte is 0 are not touched (mask may be null).
+hipError_t launch_merge_state_masked(void* v, float* s, const void* v_other,
+                                     const float* s_other, const uint8_t* mask, int64_t rows,
+                                     int H, int D, int dt, hipStream_t stream);
+
+hipError_t launch_merge_sink(const void* v, const float* s, const float* sink, void* vo,
+                             float* so, int64_t rows, int H, int D, int dt_in, int dt_out,
+                             hipStream_t stream);
+
+// Segments [indptr[p], indptr[p+1]) of v [total, H, D]; indptr null: N states per position.
+hipError_t launch_merge_segments(const void* v, const float* s, const int32_t* indptr,
+                                 int64_t total, int N, void* vo, float* so, int64_t S, int H,
+                                 int D, int dt_in, int dt_out, hipStream_t stream);
+
 hipError_t launch_split_kv_partial(const void* q, const void* kc, const void* vc,
                                    const int32_t* page_table, int pt_stride,
                                    const int32_t* ctx_lens, int B, int Hq, int Hkv,
@@ -20,6 +34,16 @@ hipError_t launch_split_kv_partial(const void* q, const void* kc, const void* vc
                                    int kv_dtype, float* o_part, float* lse_part,
                                    hipStream_t stream, int32_t* counters = nullptr,
                                    void* o = nullptr, float* lse = nullptr, int out_dtype = -1);
+
+// Per-sequence split counts (split_indptr [B+1] on the device). counters null:
+// pass 1 only; otherwise pass 1 fused with the combine.
+hipError_t launch_split_kv_partial_varlen(const void* q, const void* kc, const void* vc,
+                                          const int32_t* page_table, int pt_stride,
+                                          const int32_t* ctx_lens, int B, int Hq, int Hkv,
+                                          int64_t num_phys_pages, const int32_t* split_indptr,
+                                          int total_splits, float sm_scale, int kv_dtype,
+                                          float* o_part, float* lse_part, hipStream_t stream,
+                                          int32_t* counters, void* o, float* lse, int out_dtype);
 
 // Cascade prefix: chunk count and chunk length (tokens) for a shape.
 void prefix_attention_plan(int R, int Hq, int Hkv, int prefix_len, int* n_chunks,

@@ -10,6 +10,15 @@
 // use the max-based guard so that -inf - (-inf) gives weight 0; a state of
 // weight 0 is skipped by select (its v may hold anything); the normaliser uses
 // 1/Z or 0 when Z = 0, so an all-empty row writes v = 0, s = -inf.
+//
+// The two-state kernel has two more modes: a per-position mask (positions
+// whose mask byte is 0 are left untouched: merge_state_in_place, section 7),
+// and the attention sink, a second state (0, sink * log2 e) per head
+// ("FlashAttention's empty-row LSE", table of section 0, FlashMLA branch of section 2.1).
+// The segmented kernel merges index sets of any size, one wave or more per
+// (position, head): variable-length segments given by an index pointer array,
+// or N states per position when N is too large for the N-state kernel's
+// one-pass layout (section 7's "many index sets" variant).
 #include "common.h"
 #include "launch.h"
 
@@ -27,16 +36,28 @@ int next_pow2(int x) {
 }
 
 // Two states. Lanes per row L = 2^lanes_shift >= D/8; a block covers 256/L rows.
-template <int DTI, int DTO>
+// MODE: kPlain; kMasked (mask [rows / H] bytes, 0 = keep state a untouched);
+// kSink (state b is (0, sink[row % H] * log2 e); vb and sb are unused).
+enum { kPlain = 0, kMasked = 1, kSink = 2 };
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int DTI, int DTO, int MODE>
 __global__ __launch_bounds__(kBlock) void merge_state_kernel(
     const void* va, const float* sa, const void* vb, const float* sb, void* vo, float* so,
-    int64_t rows, int D, int lanes_shift) {
+    int64_t rows, int D, int lanes_shift, const uint8_t* mask, const float* sink, int H) {
   const int lane_in_row = threadIdx.x & ((1 << lanes_shift) - 1);
   const int64_t row =
       static_cast<int64_t>(blockIdx.x) * (kBlock >> lanes_shift) + (threadIdx.x >> lanes_shift);
   if (row >= rows) return;
+  if constexpr (MODE == kMasked) {
+    if (mask[row / H] == 0) return;
+  }
   const float a = sanitize_lse(sa[row]);
-  const float b = sanitize_lse(sb[row]);
+  float b;
+  if constexpr (MODE == kSink)
+    b = sanitize_lse(sink[row % H] * kLog2e);
+  else
+    b = sanitize_lse(sb[row]);
   const float m = __builtin_fmaxf(a, b);
   const float wa = guarded_exp2(a - m);
   const float wb = guarded_exp2(b - m);
@@ -46,13 +67,13 @@ __global__ __launch_bounds__(kBlock) void merge_state_kernel(
     const int64_t off = row * D + d0;
     float xa[8], xb[8], y[8];
     load8<DTI>(va, off, xa);
-    load8<DTI>(vb, off, xb);
+    if constexpr (MODE != kSink) load8<DTI>(vb, off, xb);
     const float inv = guarded_inv(z);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       // Two rounded products and one add: the same bits for (a, b) and (b, a).
       const float ta = (wa > 0.0f) ? wa * xa[j] : 0.0f;
-      const float tb = (wb > 0.0f) ? wb * xb[j] : 0.0f;
+      const float tb = (MODE != kSink && wb > 0.0f) ? wb * xb[j] : 0.0f;
       y[j] = (ta + tb) * inv;
     }
     store8<DTO>(vo, off, y);
@@ -169,22 +190,207 @@ __global__ __launch_bounds__(kBlock) void merge_states_kernel(
   if (so != nullptr && lane_in_row == 0) so[row] = m + hw_log2(z);
 }
 
-template <int DTI>
+template <int DTI, int MODE>
 hipError_t merge_state_out(int dt_out, const void* va, const float* sa, const void* vb,
                            const float* sb, void* vo, float* so, int64_t rows, int D,
-                           int lanes_shift, dim3 grid, hipStream_t st) {
+                           int lanes_shift, const uint8_t* mask, const float* sink, int H,
+                           dim3 grid, hipStream_t st) {
   switch (dt_out) {
     case MI_F16:
-      merge_state_kernel<DTI, MI_F16><<<grid, kBlock, 0, st>>>(va, sa, vb, sb, vo, so, rows, D, lanes_shift);
+      merge_state_kernel<DTI, MI_F16, MODE><<<grid, kBlock, 0, st>>>(va, sa, vb, sb, vo, so, rows, D, lanes_shift, mask, sink, H);
       break;
     case MI_BF16:
-      merge_state_kernel<DTI, MI_BF16><<<grid, kBlock, 0, st>>>(va, sa, vb, sb, vo, so, rows, D, lanes_shift);
+      merge_state_kernel<DTI, MI_BF16, MODE><<<grid, kBlock, 0, st>>>(va, sa, vb, sb, vo, so, rows, D, lanes_shift, mask, sink, H);
       break;
     default:
-      merge_state_kernel<DTI, MI_F32><<<grid, kBlock, 0, st>>>(va, sa, vb, sb, vo, so, rows, D, lanes_shift);
+      merge_state_kernel<DTI, MI_F32, MODE><<<grid, kBlock, 0, st>>>(va, sa, vb, sb, vo, so, rows, D, lanes_shift, mask, sink, H);
       break;
   }
   return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t merge_state_mode(const void* va, const float* sa, const void* vb, const float* sb,
+                            void* vo, float* so, int64_t rows, int D, int dt_in, int dt_out,
+                            const uint8_t* mask, const float* sink, int H, hipStream_t st) {
+  const int lanes_shift = log2_int(next_pow2(D / 8));
+  const int64_t rows_per_block = kBlock >> lanes_shift;
+  const dim3 grid(static_cast<unsigned>((rows + rows_per_block - 1) / rows_per_block));
+  switch (dt_in) {
+    case MI_F16: return merge_state_out<MI_F16, MODE>(dt_out, va, sa, vb, sb, vo, so, rows, D, lanes_shift, mask, sink, H, grid, st);
+    case MI_BF16: return merge_state_out<MI_BF16, MODE>(dt_out, va, sa, vb, sb, vo, so, rows, D, lanes_shift, mask, sink, H, grid, st);
+    default: return merge_state_out<MI_F32, MODE>(dt_out, va, sa, vb, sb, vo, so, rows, D, lanes_shift, mask, sink, H, grid, st);
+  }
+}
+
+// Segmented merge: row (pos, h) merges the states start..end-1 of v [total, H, D],
+// s [total, H], where [start, end) = [indptr[pos], indptr[pos+1]) clamped to
+// [0, total], or [pos*N, (pos+1)*N) when indptr is null (the N-state layout
+// [S, N, H, D] is the same memory). W = 2^waves_shift waves serve a row; in a
+// wave, L = 2^lanes_shift lanes cover one state's D and the 64/L lane groups
+// take different states. A lane keeps K states' loads in flight, folds them
+// into its running (m, z, acc), then the groups merge across lanes and the
+// waves through LDS.
+constexpr int kSegMaxD = 512;
+
+template <int DTI, int DTO, int K>
+__global__ __launch_bounds__(kBlock) void merge_segments_kernel(
+    const void* __restrict__ v, const float* __restrict__ s, const int32_t* __restrict__ indptr,
+    int64_t total, int N, void* __restrict__ vo, float* __restrict__ so, int64_t rows, int H,
+    int D, int lanes_shift, int waves_shift) {
+  __shared__ float lds_acc[kBlock / 64][kSegMaxD];
+  __shared__ float lds_mz[kBlock / 64][2];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int L = 1 << lanes_shift;
+  const int SG = 64 >> lanes_shift;
+  const int W = 1 << waves_shift;
+  const int wr = wave & (W - 1);
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * ((kBlock / 64) >> waves_shift) +
+                      (wave >> waves_shift);
+  const bool row_ok = row < rows;
+  const int c = lane & (L - 1);
+  const int sg = lane >> lanes_shift;
+  const int d0 = c * 8;
+  const bool lane_ok = d0 < D;
+  const int64_t pos = row_ok ? row / H : 0;
+  const int h = row_ok ? static_cast<int>(row - pos * H) : 0;
+  int64_t start = 0, end = 0;
+  if (row_ok) {
+    if (indptr != nullptr) {
+      start = indptr[pos];
+      end = indptr[pos + 1];
+      start = start < 0 ? 0 : (start > total ? total : start);
+      end = end < start ? start : (end > total ? total : end);
+    } else {
+      start = pos * N;
+      end = start + N;
+    }
+  }
+  const int64_t n = end - start;
+
+  float m = -kInf, z = 0.0f, acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+  const int step = SG * W;
+  for (int64_t k0 = sg + SG * wr; k0 < n; k0 += static_cast<int64_t>(step) * K) {
+    float sv[K], x[K][8];
+    // Unconditional loads at clamped indices, selected afterwards (a masked
+    // load followed by a zero-fill would wait after every load).
+#pragma unroll
+    for (int u = 0; u < K; ++u) {
+      const int64_t k = k0 + static_cast<int64_t>(u) * step;
+      const int64_t idx = (start + (k < n ? k : 0)) * H + h;
+      sv[u] = s[idx];
+      load8<DTI>(v, idx * D + (lane_ok ? d0 : 0), x[u]);
+    }
+    float cm = m;
+#pragma unroll
+    for (int u = 0; u < K; ++u) {
+      sv[u] = (k0 + static_cast<int64_t>(u) * step < n) ? sanitize_lse(sv[u]) : -kInf;
+      cm = __builtin_fmaxf(cm, sv[u]);
+    }
+    const float keep = guarded_exp2(m - cm);
+    z *= keep;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] *= keep;
+#pragma unroll
+    for (int u = 0; u < K; ++u) {
+      const float w = guarded_exp2(sv[u] - cm);
+      z += w;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        acc[j] = (w > 0.0f && lane_ok) ? __builtin_fmaf(w, x[u][j], acc[j]) : acc[j];
+    }
+    m = cm;
+  }
+  // Merge the lane groups of the wave (lanes c, c + L, c + 2L, ...).
+  for (int sh = L; sh < 64; sh <<= 1) {
+    const float mo = shfl_xor(m, sh);
+    const float zo = shfl_xor(z, sh);
+    const float M = __builtin_fmaxf(m, mo);
+    const float ws = guarded_exp2(m - M);
+    const float wo = guarded_exp2(mo - M);
+    z = z * ws + zo * wo;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float ao = shfl_xor(acc[j], sh);
+      acc[j] = (ws > 0.0f ? acc[j] * ws : 0.0f) + (wo > 0.0f ? ao * wo : 0.0f);
+    }
+    m = M;
+  }
+  if (W > 1) {
+    if (sg == 0 && lane_ok) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) lds_acc[wave][d0 + j] = acc[j];
+    }
+    if (lane == 0) {
+      lds_mz[wave][0] = m;
+      lds_mz[wave][1] = z;
+    }
+    __syncthreads();
+    if (wr != 0) return;
+    const int w0 = wave;  // the row's first wave
+    float M = -kInf;
+    for (int k = 0; k < W; ++k) M = __builtin_fmaxf(M, lds_mz[w0 + k][0]);
+    z = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+    for (int k = 0; k < W; ++k) {
+      const float w = guarded_exp2(lds_mz[w0 + k][0] - M);
+      z = __builtin_fmaf(w, lds_mz[w0 + k][1], z);
+      if (w > 0.0f && lane_ok) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = __builtin_fmaf(w, lds_acc[w0 + k][d0 + j], acc[j]);
+      }
+    }
+    m = M;
+  }
+  if (!row_ok || sg != 0) return;
+  if (lane_ok) {
+    const float inv = guarded_inv(z);
+    float y[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = acc[j] * inv;
+    store8<DTO>(vo, row * D + d0, y);
+  }
+  if (so != nullptr && c == 0) so[row] = m + hw_log2(z);
+}
+
+template <int DTI, int DTO>
+hipError_t merge_segments_k(int K, dim3 grid, hipStream_t st, const void* v, const float* s,
+                            const int32_t* indptr, int64_t total, int N, void* vo, float* so,
+                            int64_t rows, int H, int D, int lanes_shift, int waves_shift) {
+  switch (K) {
+    case 1:
+      merge_segments_kernel<DTI, DTO, 1><<<grid, kBlock, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, waves_shift);
+      break;
+    case 2:
+      merge_segments_kernel<DTI, DTO, 2><<<grid, kBlock, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, waves_shift);
+      break;
+    case 4:
+      merge_segments_kernel<DTI, DTO, 4><<<grid, kBlock, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, waves_shift);
+      break;
+    default:
+      merge_segments_kernel<DTI, DTO, 8><<<grid, kBlock, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, waves_shift);
+      break;
+  }
+  return hipGetLastError();
+}
+
+template <int DTI>
+hipError_t merge_segments_out(int dt_out, int K, dim3 grid, hipStream_t st, const void* v,
+                              const float* s, const int32_t* indptr, int64_t total, int N,
+                              void* vo, float* so, int64_t rows, int H, int D, int lanes_shift,
+                              int waves_shift) {
+  switch (dt_out) {
+    case MI_F16:
+      return merge_segments_k<DTI, MI_F16>(K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, waves_shift);
+    case MI_BF16:
+      return merge_segments_k<DTI, MI_BF16>(K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, waves_shift);
+    default:
+      return merge_segments_k<DTI, MI_F32>(K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, waves_shift);
+  }
 }
 
 template <int DTI, int DTO>
@@ -227,13 +433,49 @@ hipError_t merge_states_out(int dt_out, int chunk, const void* v, const float* s
 hipError_t launch_merge_state(const void* va, const float* sa, const void* vb, const float* sb,
                               void* vo, float* so, int64_t rows, int D, int dt_in, int dt_out,
                               hipStream_t st) {
+  return merge_state_mode<kPlain>(va, sa, vb, sb, vo, so, rows, D, dt_in, dt_out, nullptr,
+                                  nullptr, 1, st);
+}
+
+hipError_t launch_merge_state_masked(void* v, float* s, const void* v_other,
+                                     const float* s_other, const uint8_t* mask, int64_t rows,
+                                     int H, int D, int dt, hipStream_t st) {
+  if (mask == nullptr)
+    return merge_state_mode<kPlain>(v, s, v_other, s_other, v, s, rows, D, dt, dt, nullptr,
+                                    nullptr, H, st);
+  return merge_state_mode<kMasked>(v, s, v_other, s_other, v, s, rows, D, dt, dt, mask, nullptr,
+                                   H, st);
+}
+
+hipError_t launch_merge_sink(const void* v, const float* s, const float* sink, void* vo,
+                             float* so, int64_t rows, int H, int D, int dt_in, int dt_out,
+                             hipStream_t st) {
+  return merge_state_mode<kSink>(v, s, nullptr, nullptr, vo, so, rows, D, dt_in, dt_out,
+                                 nullptr, sink, H, st);
+}
+
+hipError_t launch_merge_segments(const void* v, const float* s, const int32_t* indptr,
+                                 int64_t total, int N, void* vo, float* so, int64_t S, int H,
+                                 int D, int dt_in, int dt_out, hipStream_t st) {
+  const int64_t rows = S * H;
   const int lanes_shift = log2_int(next_pow2(D / 8));
-  const int64_t rows_per_block = kBlock >> lanes_shift;
+  const int SG = 64 >> lanes_shift;
+  // States per row on average; waves per row: enough waves in flight for the
+  // device (about 16 per CU) when rows are few, but no wave without a state.
+  const int64_t avg = indptr != nullptr ? (S > 0 ? (total + S - 1) / S : 0) : N;
+  constexpr int64_t kTargetWaves = 4096;
+  int W = 1;
+  while (W < kBlock / 64 && rows * W < kTargetWaves && static_cast<int64_t>(SG) * W * 2 <= avg)
+    W *= 2;
+  const int waves_shift = log2_int(W);
+  const int64_t per_lane = (avg + SG * W - 1) / (SG * W);
+  const int K = per_lane >= 8 ? 8 : next_pow2(static_cast<int>(per_lane > 0 ? per_lane : 1));
+  const int64_t rows_per_block = (kBlock / 64) >> waves_shift;
   const dim3 grid(static_cast<unsigned>((rows + rows_per_block - 1) / rows_per_block));
   switch (dt_in) {
-    case MI_F16: return merge_state_out<MI_F16>(dt_out, va, sa, vb, sb, vo, so, rows, D, lanes_shift, grid, st);
-    case MI_BF16: return merge_state_out<MI_BF16>(dt_out, va, sa, vb, sb, vo, so, rows, D, lanes_shift, grid, st);
-    default: return merge_state_out<MI_F32>(dt_out, va, sa, vb, sb, vo, so, rows, D, lanes_shift, grid, st);
+    case MI_F16: return merge_segments_out<MI_F16>(dt_out, K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, waves_shift);
+    case MI_BF16: return merge_segments_out<MI_BF16>(dt_out, K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, waves_shift);
+    default: return merge_segments_out<MI_F32>(dt_out, K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, waves_shift);
   }
 }
 

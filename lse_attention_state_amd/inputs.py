@@ -166,3 +166,24 @@ def cascade_case(seed: int, R: int = 64, prefix_len: int = 8192, suffix_len: int
             "full_lens": np.full(R, prefix_len + suffix_len, np.int32),
             "R": R, "Hq": Hq, "Hkv": Hkv, "D": D, "page": page, "dtype": dtype,
             "sm_scale": 1.0 / math.sqrt(D)}
+
+
+# ----------------------------------------------------------------------------- sink, mask, segments
+
+def sink_logits(seed: int, H: int, lo: float = -8.0, hi: float = 8.0) -> np.ndarray:
+    """One attention-sink logit per head (natural-log units), fp32 [H]."""
+    return rng(seed).uniform(lo, hi, size=H).astype(np.float32)
+
+
+def position_mask(seed: int, S: int, frac_on: float = 0.5) -> np.ndarray:
+    """uint8 [S]: 1 where a position is merged, 0 where it is left alone."""
+    return (rng(seed).random(S) < frac_on).astype(np.uint8)
+
+
+def segment_indptr(seed: int, S: int, max_len: int, empty_frac: float = 0.1) -> np.ndarray:
+    """int32 [S+1] running sums of segment lengths ~ U[1, max_len], with
+    ``empty_frac`` of the segments empty."""
+    g = rng(seed)
+    lens = g.integers(1, max_len + 1, size=S)
+    lens[g.random(S) < empty_frac] = 0
+    return np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
