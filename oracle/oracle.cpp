@@ -22,7 +22,7 @@
 //    split; section 4: an empty split writes (o = 0, lse = -inf); section 6: the
 //    rule of thumb for the number of splits, and plan() giving sequences of
 //    different lengths different numbers of splits.
-//  * "FlashAttention's empty-row LSE", section 0.1 (table) and section 1: an
+//  * "FlashAttention's empty-row LSE", section 0 (table) and section 2.1: an
 //    attention sink rescales the output by e^L / (e^L + e^sink) and adds the
 //    sink to the LSE, i.e. it is a key of logit `sink` and value 0.
 //  * "F2 hints", section 7: merge_state_in_place (here with a per-position
@@ -335,7 +335,7 @@ int or_split_partials(const void* q, int q_dtype, const void* k_cache, const voi
   return 0;
 }
 
-// Attention sink ("FlashAttention's empty-row LSE", section 0.1 and section 1):
+// Attention sink ("FlashAttention's empty-row LSE", section 0 and section 2.1):
 // the sink of head h is a key with logit sink[h] (natural units) and value 0,
 // i.e. the state (v = 0, s = sink[h] / ln 2); the result is the merge of the
 // row's state with it. The sink is sanitised like any LSE (NaN, +inf -> no
