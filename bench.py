@@ -47,6 +47,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--sweep", action="store_true",
+                    help=("instead of the step: split-count sweep over the page's three decode "
+                          "workloads and the mixed batch (uniform and per-sequence plans), "
+                          "plus the merge variants; prints a markdown report"))
     return ap.parse_args()
 
 
@@ -297,6 +301,157 @@ def cpu_baseline(host, oracle):
                        f"{dt:.2f} s wall; GB/s counts the same algorithmic bytes as the GPU")}
 
 
+def _median_us(torch, fn, iters, warmup=5):
+    """Median of per-call HIP-event durations (µs) on the current stream."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = []
+    for i in range(iters):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn(i)
+        b.record()
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    return float(np.median([1000.0 * a.elapsed_time(b) for a, b in ev]))
+
+
+def sweep(torch, mi, inputs, iters):
+    """Split-count sweep ("L3 hints", section 6 table: 1 x 32768, 8 x 4096,
+    64 x 1024 with 1/4/16/64 splits) plus the mixed batch, under the uniform and
+    the per-sequence plans, and the merge variants. K/V are rotated over 4
+    copies (512 MiB) so every call streams from HBM."""
+    import ctypes
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    Hq, Hkv, D, PAGE = 32, 8, 128, 16
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = ["# Split-count sweep and merge variants (fp16 decode, Hq=32, Hkv=8, D=128, PAGE=16)",
+           "", f"Device compute units: {cus}. Median of {iters} calls, HIP events, K/V rotated "
+           "over 4 copies. GB/s counts valid K/V tokens once plus the partials written and read.",
+           ""]
+    workloads = [("1 x 32768", np.array([32768], np.int32)),
+                 ("8 x 4096", np.full(8, 4096, np.int32)),
+                 ("64 x 1024", np.full(64, 1024, np.int32)),
+                 ("mixed 32 x U[1,8192]", inputs.mixed_ctx_lens(1004, 32))]
+    out += ["| workload | plan | splits (total) | two launches µs | one launch µs | one launch GB/s |",
+            "|---|---|---:|---:|---:|---:|"]
+    for wi, (name, ctx) in enumerate(workloads):
+        case = inputs.paged_kv_case(2000 + wi, ctx, Hq, Hkv, D, PAGE, dtype="f16")
+        B = len(ctx)
+        q = to_dev(case["q"], "f16", torch)
+        k0, v0 = to_dev(case["k"], "f16", torch), to_dev(case["v"], "f16", torch)
+        kv = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(3)]
+        pt = torch.from_numpy(case["page_table"]).cuda()
+        ctxd = torch.from_numpy(ctx).cuda()
+        P = case["k"].shape[0]
+        scale = float(case["sm_scale"])
+        kv_bytes = int(ctx.astype(np.int64).sum()) * Hkv * D * 2 * 2
+        o = torch.empty((B, Hq, D), dtype=torch.float16, device="cuda")
+        lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+        cnt = torch.zeros((B, Hkv), dtype=torch.int32, device="cuda")
+        pick = mi.plan_splits(ctx, Hkv, PAGE)
+        rows = []
+        for n in (1, 4, 16, 64):
+            op = torch.empty((B, Hq, n, D), dtype=torch.float32, device="cuda")
+            lp = torch.empty((B, Hq, n), dtype=torch.float32, device="cuda")
+            two = [Raw(mi, "mi_split_kv_decode", q, k, v, pt, pt.shape[1], ctxd, B, Hq, Hkv, D,
+                       PAGE, P, n, scale, mi.MI_F16, op, lp, o, lse, mi.MI_F16, st) for k, v in kv]
+            one = [Raw(mi, "mi_split_kv_decode_fused", q, k, v, pt, pt.shape[1], ctxd, B, Hq, Hkv,
+                       D, PAGE, P, n, scale, mi.MI_F16, op, lp, cnt, o, lse, mi.MI_F16, st)
+                   for k, v in kv]
+            t2 = _median_us(torch, lambda i: two[i % 4](), iters)
+            t1 = _median_us(torch, lambda i: one[i % 4](), iters)
+            part = B * Hq * n * (D + 1) * 4 * 2 if n > 1 else 0
+            label = "uniform" + (" (planner's pick)" if n == pick else "")
+            rows.append(f"| {name} | {label} | {n} | {t2:.1f} | {t1:.1f} | "
+                        f"{(kv_bytes + part) / (t1 * 1e-6) / 1e9:.0f} |")
+        indptr = mi.plan_splits_varlen(ctx, Hkv, PAGE)
+        total = int(indptr[-1])
+        ipd = torch.from_numpy(indptr).cuda()
+        op = torch.empty((total, Hq, D), dtype=torch.float32, device="cuda")
+        lp = torch.empty((total, Hq), dtype=torch.float32, device="cuda")
+        vtwo = [Raw(mi, "mi_split_kv_decode_varlen", q, k, v, pt, pt.shape[1], ctxd, B, Hq, Hkv, D,
+                    PAGE, P, ipd, total, scale, mi.MI_F16, op, lp, None, o, lse, mi.MI_F16, st)
+                for k, v in kv]
+        vone = [Raw(mi, "mi_split_kv_decode_varlen", q, k, v, pt, pt.shape[1], ctxd, B, Hq, Hkv, D,
+                    PAGE, P, ipd, total, scale, mi.MI_F16, op, lp, cnt, o, lse, mi.MI_F16, st)
+                for k, v in kv]
+        t2 = _median_us(torch, lambda i: vtwo[i % 4](), iters)
+        t1 = _median_us(torch, lambda i: vone[i % 4](), iters)
+        counts = np.diff(indptr)
+        part = Hq * total * (D + 1) * 4 * 2 if total > B else 0
+        rows.append(f"| {name} | per-sequence (counts {counts.min()}..{counts.max()}) | "
+                    f"({total}) | {t2:.1f} | {t1:.1f} | {(kv_bytes + part) / (t1 * 1e-6) / 1e9:.0f} |")
+        out += rows
+        del kv, k0, v0
+        torch.cuda.empty_cache()
+
+    # Merges: mi_merge_states (N-state kernel; segmented kernel below 2048 rows)
+    # against mi_merge_states_varlen (always the segmented kernel) on the same data.
+    out += ["", "| merge | shape | mi_merge_states µs | mi_merge_states_varlen µs |",
+            "|---|---|---:|---:|"]
+    for S, N, H, dt in ((32, 64, 1, "f32"), (1024, 16, 1, "f32"), (4096, 4, 8, "f16"),
+                        (512, 64, 8, "f16"), (64, 1024, 1, "f32")):
+        c = inputs.merge_states_case(2100 + N, S=S, N=N, H=H, D=D, dtype=dt)
+        cop = [(to_dev(c["v"], dt, torch), torch.from_numpy(c["s"]).cuda()) for _ in range(4)]
+        vo = torch.empty((S, H, D), dtype=torch.float16, device="cuda")
+        so = torch.empty((S, H), dtype=torch.float32, device="cuda")
+        ipd = torch.from_numpy((np.arange(S + 1) * N).astype(np.int32)).cuda()
+        code = {"f16": mi.MI_F16, "bf16": mi.MI_BF16, "f32": mi.MI_F32}[dt]
+        a = [Raw(mi, "mi_merge_states", v, s, vo, so, S, N, H, D, code, mi.MI_F16, st)
+             for v, s in cop]
+        b = [Raw(mi, "mi_merge_states_varlen", v, s, ipd, S * N, vo, so, S, H, D, code, mi.MI_F16,
+                 st) for v, s in cop]
+        ta = _median_us(torch, lambda i: a[i % 4](), iters)
+        tb = _median_us(torch, lambda i: b[i % 4](), iters)
+        out.append(f"| merge_states {dt}->f16 | S={S} N={N} H={H} D={D} | {ta:.1f} | {tb:.1f} |")
+        del cop
+        torch.cuda.empty_cache()
+
+    # Sink and masked in-place merges at the two-state size (bf16 S=32768 H=32 D=128).
+    ms = inputs.merge_state_case(1002, S=32768, H=32, D=128, dtype="bf16")
+    rows_ = 32768 * 32
+    va = [to_dev(ms["va"], "bf16", torch) for _ in range(2)]
+    sa = [torch.from_numpy(ms["sa"]).cuda() for _ in range(2)]
+    vb = to_dev(ms["vb"], "bf16", torch)
+    sb = torch.from_numpy(ms["sb"]).cuda()
+    sink = torch.from_numpy(inputs.sink_logits(1103, 32)).cuda()
+    mask = torch.from_numpy(inputs.position_mask(1010, 32768)).cuda()
+    ones = torch.ones(32768, dtype=torch.uint8, device="cuda")
+    out += ["", "| kernel | shape | µs | algorithmic bytes | GB/s | % of 8 TB/s |",
+            "|---|---|---:|---:|---:|---:|"]
+    sink_calls = [Raw(mi, "mi_merge_sink", va[i], sa[i], sink, va[i], sa[i], 32768, 32, 128,
+                      mi.MI_BF16, mi.MI_BF16, st) for i in range(2)]
+    t = _median_us(torch, lambda i: sink_calls[i % 2](), iters)
+    by = rows_ * (2 * 256 + 2 * 4) + 32 * 4
+    out.append(f"| merge_sink (in place) | bf16 S=32768 H=32 D=128 | {t:.1f} | {by} | "
+               f"{by / (t * 1e-6) / 1e9:.0f} | {by / (t * 1e-6) / 8e12 * 100:.1f} |")
+    for label, m, frac in (("all set", ones, 1.0), ("half set", mask, float(mask.float().mean()))):
+        calls = [Raw(mi, "mi_merge_state_in_place", va[i], sa[i], vb, sb, m, 32768, 32, 128,
+                     mi.MI_BF16, st) for i in range(2)]
+        t = _median_us(torch, lambda i: calls[i % 2](), iters)
+        by = int(rows_ * frac) * (3 * 256 + 3 * 4) + 32768
+        out.append(f"| merge_state_in_place, mask {label} | bf16 S=32768 H=32 D=128 | {t:.1f} | "
+                   f"{by} | {by / (t * 1e-6) / 1e9:.0f} | {by / (t * 1e-6) / 8e12 * 100:.1f} |")
+    # Variable-length merge at a streaming size: 8192 sets of 0..8 fp16 states, H=8.
+    indptr = inputs.segment_indptr(2200, 8192, 8)
+    total = int(indptr[-1])
+    c = inputs.merge_states_case(2201, S=1, N=total, H=8, D=128, dtype="f16")
+    vv = [to_dev(c["v"].reshape(total, 8, 128), "f16", torch) for _ in range(2)]
+    ss = torch.from_numpy(c["s"].reshape(total, 8)).cuda()
+    ipd = torch.from_numpy(indptr).cuda()
+    vo = torch.empty((8192, 8, 128), dtype=torch.float16, device="cuda")
+    so = torch.empty((8192, 8), dtype=torch.float32, device="cuda")
+    calls = [Raw(mi, "mi_merge_states_varlen", vv[i], ss, ipd, total, vo, so, 8192, 8, 128,
+                 mi.MI_F16, mi.MI_F16, st) for i in range(2)]
+    t = _median_us(torch, lambda i: calls[i % 2](), iters)
+    by = total * 8 * (256 + 4) + 8193 * 4 + 8192 * 8 * (256 + 4)
+    out.append(f"| merge_states_varlen | f16 8192 sets x U[0..8] states ({total}), H=8 D=128 | "
+               f"{t:.1f} | {by} | {by / (t * 1e-6) / 1e9:.0f} | {by / (t * 1e-6) / 8e12 * 100:.1f} |")
+    print("\n".join(out))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -316,6 +471,10 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 5}))
+        return
+
+    if args.sweep:
+        sweep(torch, mi, inputs, max(args.steps, 20))
         return
 
     parts, host = build_workload(torch, mi, inputs)

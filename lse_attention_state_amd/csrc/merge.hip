@@ -226,31 +226,33 @@ hipError_t merge_state_mode(const void* va, const float* sa, const void* vb, con
 // Segmented merge: row (pos, h) merges the states start..end-1 of v [total, H, D],
 // s [total, H], where [start, end) = [indptr[pos], indptr[pos+1]) clamped to
 // [0, total], or [pos*N, (pos+1)*N) when indptr is null (the N-state layout
-// [S, N, H, D] is the same memory). W = 2^waves_shift waves serve a row; in a
-// wave, L = 2^lanes_shift lanes cover one state's D and the 64/L lane groups
-// take different states. A lane keeps K states' loads in flight, folds them
-// into its running (m, z, acc), then the groups merge across lanes and the
-// waves through LDS.
+// [S, N, H, D] is the same memory). A row is served by a team of
+// T = 2^team_shift lanes: G = T / L lane groups of L = 2^lanes_shift lanes,
+// each group covering one state's D and taking states g, g + G, ... Short
+// segments get small teams (several rows per wave, like the N-state kernel);
+// long ones get teams of up to 16 waves, so even a few rows with thousands of
+// states keep the device's memory pipeline full. A lane keeps K states' loads
+// in flight and folds them into its running (m, z, acc); the groups then merge
+// across lanes, and the waves of a team through LDS.
+constexpr int kSegThreads = 1024;
 constexpr int kSegMaxD = 512;
 
 template <int DTI, int DTO, int K>
-__global__ __launch_bounds__(kBlock) void merge_segments_kernel(
+__global__ __launch_bounds__(kSegThreads) void merge_segments_kernel(
     const void* __restrict__ v, const float* __restrict__ s, const int32_t* __restrict__ indptr,
     int64_t total, int N, void* __restrict__ vo, float* __restrict__ so, int64_t rows, int H,
-    int D, int lanes_shift, int waves_shift) {
-  __shared__ float lds_acc[kBlock / 64][kSegMaxD];
-  __shared__ float lds_mz[kBlock / 64][2];
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
+    int D, int lanes_shift, int team_shift) {
+  __shared__ float lds_acc[kSegThreads / 64][kSegMaxD];
+  __shared__ float lds_mz[kSegThreads / 64][2];
   const int L = 1 << lanes_shift;
-  const int SG = 64 >> lanes_shift;
-  const int W = 1 << waves_shift;
-  const int wr = wave & (W - 1);
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * ((kBlock / 64) >> waves_shift) +
-                      (wave >> waves_shift);
+  const int T = 1 << team_shift;
+  const int G = T >> lanes_shift;
+  const int t = threadIdx.x & (T - 1);
+  const int c = t & (L - 1);
+  const int g = t >> lanes_shift;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * (kSegThreads >> team_shift) +
+                      (threadIdx.x >> team_shift);
   const bool row_ok = row < rows;
-  const int c = lane & (L - 1);
-  const int sg = lane >> lanes_shift;
   const int d0 = c * 8;
   const bool lane_ok = d0 < D;
   const int64_t pos = row_ok ? row / H : 0;
@@ -272,14 +274,13 @@ __global__ __launch_bounds__(kBlock) void merge_segments_kernel(
   float m = -kInf, z = 0.0f, acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-  const int step = SG * W;
-  for (int64_t k0 = sg + SG * wr; k0 < n; k0 += static_cast<int64_t>(step) * K) {
+  for (int64_t k0 = g; k0 < n; k0 += static_cast<int64_t>(G) * K) {
     float sv[K], x[K][8];
     // Unconditional loads at clamped indices, selected afterwards (a masked
     // load followed by a zero-fill would wait after every load).
 #pragma unroll
     for (int u = 0; u < K; ++u) {
-      const int64_t k = k0 + static_cast<int64_t>(u) * step;
+      const int64_t k = k0 + static_cast<int64_t>(u) * G;
       const int64_t idx = (start + (k < n ? k : 0)) * H + h;
       sv[u] = s[idx];
       load8<DTI>(v, idx * D + (lane_ok ? d0 : 0), x[u]);
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(kBlock) void merge_segments_kernel(
     float cm = m;
 #pragma unroll
     for (int u = 0; u < K; ++u) {
-      sv[u] = (k0 + static_cast<int64_t>(u) * step < n) ? sanitize_lse(sv[u]) : -kInf;
+      sv[u] = (k0 + static_cast<int64_t>(u) * G < n) ? sanitize_lse(sv[u]) : -kInf;
       cm = __builtin_fmaxf(cm, sv[u]);
     }
     const float keep = guarded_exp2(m - cm);
@@ -304,8 +305,9 @@ __global__ __launch_bounds__(kBlock) void merge_segments_kernel(
     }
     m = cm;
   }
-  // Merge the lane groups of the wave (lanes c, c + L, c + 2L, ...).
-  for (int sh = L; sh < 64; sh <<= 1) {
+  // Merge the lane groups inside each wave (lanes c, c + L, c + 2L, ... of the team).
+  const int in_wave = T < 64 ? T : 64;
+  for (int sh = L; sh < in_wave; sh <<= 1) {
     const float mo = shfl_xor(m, sh);
     const float zo = shfl_xor(z, sh);
     const float M = __builtin_fmaxf(m, mo);
@@ -313,14 +315,15 @@ __global__ __launch_bounds__(kBlock) void merge_segments_kernel(
     const float wo = guarded_exp2(mo - M);
     z = z * ws + zo * wo;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float ao = shfl_xor(acc[j], sh);
-      acc[j] = (ws > 0.0f ? acc[j] * ws : 0.0f) + (wo > 0.0f ? ao * wo : 0.0f);
-    }
+    for (int j = 0; j < 8; ++j) acc[j] = acc[j] * ws + shfl_xor(acc[j], sh) * wo;
     m = M;
   }
-  if (W > 1) {
-    if (sg == 0 && lane_ok) {
+  if (T > 64) {
+    // Teams of several waves: each wave's lanes of group 0 (t < L within the
+    // wave) hold the wave's merge; the team's first wave folds them.
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    if (lane < L && lane_ok) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) lds_acc[wave][d0 + j] = acc[j];
     }
@@ -329,24 +332,24 @@ __global__ __launch_bounds__(kBlock) void merge_segments_kernel(
       lds_mz[wave][1] = z;
     }
     __syncthreads();
-    if (wr != 0) return;
-    const int w0 = wave;  // the row's first wave
+    const int W = T >> 6;
+    if ((wave & (W - 1)) != 0) return;
     float M = -kInf;
-    for (int k = 0; k < W; ++k) M = __builtin_fmaxf(M, lds_mz[w0 + k][0]);
+    for (int k = 0; k < W; ++k) M = __builtin_fmaxf(M, lds_mz[wave + k][0]);
     z = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
     for (int k = 0; k < W; ++k) {
-      const float w = guarded_exp2(lds_mz[w0 + k][0] - M);
-      z = __builtin_fmaf(w, lds_mz[w0 + k][1], z);
+      const float w = guarded_exp2(lds_mz[wave + k][0] - M);
+      z = __builtin_fmaf(w, lds_mz[wave + k][1], z);
       if (w > 0.0f && lane_ok) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = __builtin_fmaf(w, lds_acc[w0 + k][d0 + j], acc[j]);
+        for (int j = 0; j < 8; ++j) acc[j] = __builtin_fmaf(w, lds_acc[wave + k][d0 + j], acc[j]);
       }
     }
     m = M;
   }
-  if (!row_ok || sg != 0) return;
+  if (!row_ok || g != 0) return;
   if (lane_ok) {
     const float inv = guarded_inv(z);
     float y[8];
@@ -360,19 +363,19 @@ __global__ __launch_bounds__(kBlock) void merge_segments_kernel(
 template <int DTI, int DTO>
 hipError_t merge_segments_k(int K, dim3 grid, hipStream_t st, const void* v, const float* s,
                             const int32_t* indptr, int64_t total, int N, void* vo, float* so,
-                            int64_t rows, int H, int D, int lanes_shift, int waves_shift) {
+                            int64_t rows, int H, int D, int lanes_shift, int team_shift) {
   switch (K) {
     case 1:
-      merge_segments_kernel<DTI, DTO, 1><<<grid, kBlock, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, waves_shift);
+      merge_segments_kernel<DTI, DTO, 1><<<grid, kSegThreads, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
       break;
     case 2:
-      merge_segments_kernel<DTI, DTO, 2><<<grid, kBlock, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, waves_shift);
+      merge_segments_kernel<DTI, DTO, 2><<<grid, kSegThreads, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
       break;
     case 4:
-      merge_segments_kernel<DTI, DTO, 4><<<grid, kBlock, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, waves_shift);
+      merge_segments_kernel<DTI, DTO, 4><<<grid, kSegThreads, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
       break;
     default:
-      merge_segments_kernel<DTI, DTO, 8><<<grid, kBlock, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, waves_shift);
+      merge_segments_kernel<DTI, DTO, 8><<<grid, kSegThreads, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
       break;
   }
   return hipGetLastError();
@@ -382,14 +385,14 @@ template <int DTI>
 hipError_t merge_segments_out(int dt_out, int K, dim3 grid, hipStream_t st, const void* v,
                               const float* s, const int32_t* indptr, int64_t total, int N,
                               void* vo, float* so, int64_t rows, int H, int D, int lanes_shift,
-                              int waves_shift) {
+                              int team_shift) {
   switch (dt_out) {
     case MI_F16:
-      return merge_segments_k<DTI, MI_F16>(K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, waves_shift);
+      return merge_segments_k<DTI, MI_F16>(K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
     case MI_BF16:
-      return merge_segments_k<DTI, MI_BF16>(K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, waves_shift);
+      return merge_segments_k<DTI, MI_BF16>(K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
     default:
-      return merge_segments_k<DTI, MI_F32>(K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, waves_shift);
+      return merge_segments_k<DTI, MI_F32>(K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
   }
 }
 
@@ -458,30 +461,39 @@ hipError_t launch_merge_segments(const void* v, const float* s, const int32_t* i
                                  int64_t total, int N, void* vo, float* so, int64_t S, int H,
                                  int D, int dt_in, int dt_out, hipStream_t st) {
   const int64_t rows = S * H;
-  const int lanes_shift = log2_int(next_pow2(D / 8));
-  const int SG = 64 >> lanes_shift;
-  // States per row on average; waves per row: enough waves in flight for the
-  // device (about 16 per CU) when rows are few, but no wave without a state.
+  const int L = next_pow2(D / 8);
+  const int lanes_shift = log2_int(L);
+  // Team size from the average set size: up to 8 states in flight per lane;
+  // more lane groups when sets are longer, and more still (while each group
+  // keeps at least one state) when there are too few rows to give the device
+  // about 16 waves per compute unit.
   const int64_t avg = indptr != nullptr ? (S > 0 ? (total + S - 1) / S : 0) : N;
-  constexpr int64_t kTargetWaves = 4096;
-  int W = 1;
-  while (W < kBlock / 64 && rows * W < kTargetWaves && static_cast<int64_t>(SG) * W * 2 <= avg)
-    W *= 2;
-  const int waves_shift = log2_int(W);
-  const int64_t per_lane = (avg + SG * W - 1) / (SG * W);
+  constexpr int64_t kTargetLanes = 4096 * 64;
+  const int max_groups = kSegThreads / L;
+  int G = 1;
+  while (G < max_groups && static_cast<int64_t>(G) * 8 < avg) G *= 2;
+  while (G < max_groups && 2 * G <= avg && rows * L * G < kTargetLanes) G *= 2;
+  const int team_shift = log2_int(L * G);
+  const int64_t per_lane = (avg + G - 1) / G;
   const int K = per_lane >= 8 ? 8 : next_pow2(static_cast<int>(per_lane > 0 ? per_lane : 1));
-  const int64_t rows_per_block = (kBlock / 64) >> waves_shift;
+  const int64_t rows_per_block = kSegThreads >> team_shift;
   const dim3 grid(static_cast<unsigned>((rows + rows_per_block - 1) / rows_per_block));
   switch (dt_in) {
-    case MI_F16: return merge_segments_out<MI_F16>(dt_out, K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, waves_shift);
-    case MI_BF16: return merge_segments_out<MI_BF16>(dt_out, K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, waves_shift);
-    default: return merge_segments_out<MI_F32>(dt_out, K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, waves_shift);
+    case MI_F16: return merge_segments_out<MI_F16>(dt_out, K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
+    case MI_BF16: return merge_segments_out<MI_BF16>(dt_out, K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
+    default: return merge_segments_out<MI_F32>(dt_out, K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
   }
 }
 
 hipError_t launch_merge_states(const void* v, const float* s, void* vo, float* so, int64_t S,
                                int N, int H, int D, int dt_in, int dt_out, hipStream_t st) {
   const int64_t rows = S * H;
+  // Few rows with many states each (the split-KV combine at small batch): the
+  // segmented kernel spreads a row over up to 16 waves (measured on MI355X:
+  // S*H = 32, N = 64 fp32 in 8.4 us against 11.6; S*H = 1024, N = 16 in 8.1
+  // against 8.8); with many rows the N-state kernel's lighter merge wins.
+  if (rows < 2048 && N >= 8)
+    return launch_merge_segments(v, s, nullptr, S * N, N, vo, so, S, H, D, dt_in, dt_out, st);
   const int L = next_pow2(D / 8);
   const int lanes_shift = log2_int(L);
   // Split the N states of a row over G lane groups when rows alone would not
