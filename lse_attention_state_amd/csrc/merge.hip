@@ -234,10 +234,11 @@ hipError_t merge_state_mode(const void* va, const float* sa, const void* vb, con
 // states keep the device's memory pipeline full. A lane keeps K states' loads
 // in flight and folds them into its running (m, z, acc); the groups then merge
 // across lanes, and the waves of a team through LDS.
-constexpr int kSegThreads = 1024;
+// Block size: 256 threads while a team fits in it (more blocks per compute
+// unit), 1024 for teams of more than four waves.
 constexpr int kSegMaxD = 512;
 
-template <int DTI, int DTO, int K>
+template <int DTI, int DTO, int K, int kSegThreads>
 __global__ __launch_bounds__(kSegThreads) void merge_segments_kernel(
     const void* __restrict__ v, const float* __restrict__ s, const int32_t* __restrict__ indptr,
     int64_t total, int N, void* __restrict__ vo, float* __restrict__ so, int64_t rows, int H,
@@ -360,39 +361,51 @@ __global__ __launch_bounds__(kSegThreads) void merge_segments_kernel(
   if (so != nullptr && c == 0) so[row] = m + hw_log2(z);
 }
 
-template <int DTI, int DTO>
-hipError_t merge_segments_k(int K, dim3 grid, hipStream_t st, const void* v, const float* s,
-                            const int32_t* indptr, int64_t total, int N, void* vo, float* so,
-                            int64_t rows, int H, int D, int lanes_shift, int team_shift) {
+template <int DTI, int DTO, int kThr>
+hipError_t merge_segments_kt(int K, dim3 grid, hipStream_t st, const void* v, const float* s,
+                             const int32_t* indptr, int64_t total, int N, void* vo, float* so,
+                             int64_t rows, int H, int D, int lanes_shift, int team_shift) {
   switch (K) {
     case 1:
-      merge_segments_kernel<DTI, DTO, 1><<<grid, kSegThreads, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
+      merge_segments_kernel<DTI, DTO, 1, kThr><<<grid, kThr, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
       break;
     case 2:
-      merge_segments_kernel<DTI, DTO, 2><<<grid, kSegThreads, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
+      merge_segments_kernel<DTI, DTO, 2, kThr><<<grid, kThr, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
       break;
     case 4:
-      merge_segments_kernel<DTI, DTO, 4><<<grid, kSegThreads, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
+      merge_segments_kernel<DTI, DTO, 4, kThr><<<grid, kThr, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
       break;
     default:
-      merge_segments_kernel<DTI, DTO, 8><<<grid, kSegThreads, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
+      merge_segments_kernel<DTI, DTO, 8, kThr><<<grid, kThr, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
       break;
   }
   return hipGetLastError();
 }
 
+// The grid is given in teams; the block size follows from the team size.
+template <int DTI, int DTO>
+hipError_t merge_segments_k(int K, int64_t rows, hipStream_t st, const void* v, const float* s,
+                            const int32_t* indptr, int64_t total, int N, void* vo, float* so,
+                            int H, int D, int lanes_shift, int team_shift) {
+  const int threads = team_shift > 8 ? 1024 : 256;
+  const int64_t rows_per_block = threads >> team_shift;
+  const dim3 grid(static_cast<unsigned>((rows + rows_per_block - 1) / rows_per_block));
+  if (threads == 1024)
+    return merge_segments_kt<DTI, DTO, 1024>(K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
+  return merge_segments_kt<DTI, DTO, 256>(K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
+}
+
 template <int DTI>
-hipError_t merge_segments_out(int dt_out, int K, dim3 grid, hipStream_t st, const void* v,
+hipError_t merge_segments_out(int dt_out, int K, int64_t rows, hipStream_t st, const void* v,
                               const float* s, const int32_t* indptr, int64_t total, int N,
-                              void* vo, float* so, int64_t rows, int H, int D, int lanes_shift,
-                              int team_shift) {
+                              void* vo, float* so, int H, int D, int lanes_shift, int team_shift) {
   switch (dt_out) {
     case MI_F16:
-      return merge_segments_k<DTI, MI_F16>(K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
+      return merge_segments_k<DTI, MI_F16>(K, rows, st, v, s, indptr, total, N, vo, so, H, D, lanes_shift, team_shift);
     case MI_BF16:
-      return merge_segments_k<DTI, MI_BF16>(K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
+      return merge_segments_k<DTI, MI_BF16>(K, rows, st, v, s, indptr, total, N, vo, so, H, D, lanes_shift, team_shift);
     default:
-      return merge_segments_k<DTI, MI_F32>(K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
+      return merge_segments_k<DTI, MI_F32>(K, rows, st, v, s, indptr, total, N, vo, so, H, D, lanes_shift, team_shift);
   }
 }
 
@@ -469,19 +482,17 @@ hipError_t launch_merge_segments(const void* v, const float* s, const int32_t* i
   // about 16 waves per compute unit.
   const int64_t avg = indptr != nullptr ? (S > 0 ? (total + S - 1) / S : 0) : N;
   constexpr int64_t kTargetLanes = 4096 * 64;
-  const int max_groups = kSegThreads / L;
+  const int max_groups = 1024 / L;
   int G = 1;
   while (G < max_groups && static_cast<int64_t>(G) * 8 < avg) G *= 2;
   while (G < max_groups && 2 * G <= avg && rows * L * G < kTargetLanes) G *= 2;
   const int team_shift = log2_int(L * G);
   const int64_t per_lane = (avg + G - 1) / G;
   const int K = per_lane >= 8 ? 8 : next_pow2(static_cast<int>(per_lane > 0 ? per_lane : 1));
-  const int64_t rows_per_block = kSegThreads >> team_shift;
-  const dim3 grid(static_cast<unsigned>((rows + rows_per_block - 1) / rows_per_block));
   switch (dt_in) {
-    case MI_F16: return merge_segments_out<MI_F16>(dt_out, K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
-    case MI_BF16: return merge_segments_out<MI_BF16>(dt_out, K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
-    default: return merge_segments_out<MI_F32>(dt_out, K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
+    case MI_F16: return merge_segments_out<MI_F16>(dt_out, K, rows, st, v, s, indptr, total, N, vo, so, H, D, lanes_shift, team_shift);
+    case MI_BF16: return merge_segments_out<MI_BF16>(dt_out, K, rows, st, v, s, indptr, total, N, vo, so, H, D, lanes_shift, team_shift);
+    default: return merge_segments_out<MI_F32>(dt_out, K, rows, st, v, s, indptr, total, N, vo, so, H, D, lanes_shift, team_shift);
   }
 }
 
