@@ -312,3 +312,22 @@ def test_varlen_decode_repeated_calls_reuse_counters():
             first = (o.clone(), lse.clone())
         else:
             assert torch.equal(o, first[0]) and torch.equal(lse, first[1])
+
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("B", [63, 64, 300, 4031])
+def test_varlen_decode_many_sequences(fused, B):
+    """Batches past one 64-entry search round (B >= 64 takes the second round;
+    4031 is the largest supported), short random lengths including 0, and
+    random split counts 1..4 per sequence (so that segment boundaries fall
+    everywhere in the index array)."""
+    _say("varlen decode many sequences", B, fused)
+    g = np.random.default_rng(500 + B)
+    ctx = g.integers(0, 120, size=B).astype(np.int32)
+    ctx[g.random(B) < 0.05] = 0
+    Hq, Hkv = (8, 8) if B > 1000 else (16, 4)
+    case = inputs.paged_kv_case(501 + B, ctx, Hq, Hkv, 128, 16, dtype="bf16")
+    counts = g.integers(1, 5, size=B).astype(np.int32)
+    indptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    _say("total splits", int(indptr[-1]))
+    _check_varlen(case, indptr, fused)
