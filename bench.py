@@ -391,8 +391,9 @@ def sweep(torch, mi, inputs, iters):
     # against mi_merge_states_varlen (always the segmented kernel) on the same data.
     out += ["", "| merge | shape | mi_merge_states µs | mi_merge_states_varlen µs |",
             "|---|---|---:|---:|"]
-    for S, N, H, dt in ((32, 64, 1, "f32"), (1024, 16, 1, "f32"), (4096, 4, 8, "f16"),
-                        (512, 64, 8, "f16"), (64, 1024, 1, "f32")):
+    for S, N, H, dt in ((32, 64, 1, "f32"), (1024, 16, 1, "f32"), (2048, 16, 1, "f32"),
+                        (4096, 16, 1, "f32"), (4096, 4, 8, "f16"), (512, 64, 8, "f16"),
+                        (64, 1024, 1, "f32")):
         c = inputs.merge_states_case(2100 + N, S=S, N=N, H=H, D=D, dtype=dt)
         cop = [(to_dev(c["v"], dt, torch), torch.from_numpy(c["s"]).cuda()) for _ in range(4)]
         vo = torch.empty((S, H, D), dtype=torch.float16, device="cuda")
