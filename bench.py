@@ -317,7 +317,7 @@ def _median_us(torch, fn, iters, warmup=5):
     return float(np.median([1000.0 * a.elapsed_time(b) for a, b in ev]))
 
 
-def sweep(torch, mi, inputs, iters):
+def sweep(torch, mi, inputs, iters, with_cpu=True):
     """Split-count sweep ("L3 hints", section 6 table: 1 x 32768, 8 x 4096,
     64 x 1024 with 1/4/16/64 splits) plus the mixed batch, under the uniform and
     the per-sequence plans, and the merge variants. K/V are rotated over 4
@@ -450,7 +450,53 @@ def sweep(torch, mi, inputs, iters):
     by = total * 8 * (256 + 4) + 8193 * 4 + 8192 * 8 * (256 + 4)
     out.append(f"| merge_states_varlen | f16 8192 sets x U[0..8] states ({total}), H=8 D=128 | "
                f"{t:.1f} | {by} | {by / (t * 1e-6) / 1e9:.0f} | {by / (t * 1e-6) / 8e12 * 100:.1f} |")
+    if with_cpu:
+        import oracle
+        out += [""] + cpu_baseline_sweep(oracle, inputs, ms, sink.cpu().numpy(), indptr, c)
     print("\n".join(out))
+
+
+def cpu_baseline_sweep(oracle, inputs, ms, sink, indptr, vs_case):
+    """The fp64 oracle timed beside the sweep's kernels, on bounded samples of
+    the same inputs (cpu_baseline leg of --sweep). GB/s counts the same
+    algorithmic bytes per row as the GPU lines."""
+    threads = len(os.sched_getaffinity(0))
+    L = [f"Oracle (fp64 CPU, {threads} threads) on bounded samples of the same inputs:", "",
+         "| path | sample | s | algorithmic GB/s |", "|---|---|---:|---:|"]
+    n = 32768 * 32 // 4                       # a quarter of the two-state rows
+    va, sa = ms["va"].reshape(-1, 1, 128)[:n], ms["sa"].reshape(-1, 1)[:n]
+    vb, sb = ms["vb"].reshape(-1, 1, 128)[:n], ms["sb"].reshape(-1, 1)[:n]
+    t0 = time.perf_counter()
+    oracle.merge_sink(va, sa, sink[:1], "bf16", threads)
+    dt = time.perf_counter() - t0
+    L.append(f"| merge_sink | {n} rows (one head's sink) | {dt:.2f} | {n * 520 / dt / 1e9:.3f} |")
+    mask = np.ones(n, np.uint8)
+    t0 = time.perf_counter()
+    oracle.merge_state_masked(va, sa, vb, sb, mask, "bf16", threads)
+    dt = time.perf_counter() - t0
+    L.append(f"| merge_state_in_place (mask all set) | {n} rows | {dt:.2f} | {n * 780 / dt / 1e9:.3f} |")
+    S2 = len(indptr) - 1                      # every set
+    ip = indptr
+    tot = int(ip[-1])
+    t0 = time.perf_counter()
+    oracle.merge_states_varlen(vs_case["v"].reshape(-1, 8, 128)[:tot], vs_case["s"].reshape(-1, 8)[:tot],
+                               ip, "f16", threads)
+    dt = time.perf_counter() - t0
+    L.append(f"| merge_states_varlen | all {S2} sets ({tot} states), H=8 | {dt:.2f} | "
+             f"{(tot + S2) * 8 * 260 / dt / 1e9:.3f} |")
+    ctx = inputs.mixed_ctx_lens(1004, 32)
+    case = inputs.paged_kv_case(2003, ctx, 32, 8, 128, 16, dtype="f16")
+    args = (case["q"], case["k"], case["v"], case["page_table"], ctx, case["sm_scale"])
+    pages = -(-ctx.astype(np.int64) // 16)
+    counts = np.maximum(1, -(-pages // 64))             # splits of at most 64 pages
+    ipd = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    t0 = time.perf_counter()
+    oracle.split_partials_varlen(*args, ipd, "f16", "f16", threads)
+    dt = time.perf_counter() - t0
+    kvb = int(ctx.astype(np.int64).sum()) * 8 * 128 * 4
+    L.append(f"| per-sequence decode partials | the 32-sequence mixed batch "
+             f"({int(ctx.sum())} tokens) | {dt:.2f} | {kvb / dt / 1e9:.3f} |")
+    return L
 
 
 def main():
@@ -475,7 +521,7 @@ def main():
         return
 
     if args.sweep:
-        sweep(torch, mi, inputs, max(args.steps, 20))
+        sweep(torch, mi, inputs, max(args.steps, 20), with_cpu=not args.no_cpu_baseline)
         return
 
     parts, host = build_workload(torch, mi, inputs)
