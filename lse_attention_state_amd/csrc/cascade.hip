@@ -122,11 +122,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefix_attention_kernel(
   const int n_pages = (prefix_len + kPage - 1) / kPage;
   const int page0 = tok0 / kPage;
 
-  // The chunk's page ids, one per lane (a chunk spans at most 64 pages).
+  // The chunk's page ids, one per lane (a chunk spans at most 64 pages), and
+  // which of them hold tokens of this chunk: bit pl of ok_pages is set when
+  // chunk page pl exists, lies inside the chunk's tiles and has a valid id, so
+  // every later validity test is a scalar bit test.
   const int32_t ids = (page0 + lane < n_pages) ? prefix_pages[page0 + lane] : -1;
-  auto page_ok = [&](int pl, int32_t phys) {
-    return page0 + pl < n_pages && pl < 2 * n_tiles && phys >= 0 && phys < num_phys;
-  };
+  const uint64_t ok_pages = __builtin_amdgcn_ballot_w64(
+      page0 + lane < n_pages && lane < 2 * n_tiles && ids >= 0 && ids < num_phys);
+  auto page_ok = [&](int pl, int32_t) { return pl < 64 && ((ok_pages >> pl) & 1) != 0; };
 
   // Staging roles. K: thread (p = tid/16, c = tid%16) takes tile tokens 2p,
   // 2p+1 at d = 8c (its wave covers one page: p/8 = wave/2). V: thread
