@@ -389,8 +389,8 @@ def sweep(torch, mi, inputs, iters, with_cpu=True):
 
     # Merges: mi_merge_states (N-state kernel; segmented kernel below 2048 rows)
     # against mi_merge_states_varlen (always the segmented kernel) on the same data.
-    out += ["", "| merge | shape | mi_merge_states µs | mi_merge_states_varlen µs |",
-            "|---|---|---:|---:|"]
+    out += ["", "| merge | shape | mi_merge_states µs | mi_merge_states_varlen µs | "
+            "mi_merge_states_two_level µs |", "|---|---|---:|---:|---:|"]
     for S, N, H, dt in ((32, 64, 1, "f32"), (1024, 16, 1, "f32"), (2048, 16, 1, "f32"),
                         (4096, 16, 1, "f32"), (4096, 4, 8, "f16"), (512, 64, 8, "f16"),
                         (64, 1024, 1, "f32")):
@@ -404,9 +404,15 @@ def sweep(torch, mi, inputs, iters, with_cpu=True):
              for v, s in cop]
         b = [Raw(mi, "mi_merge_states_varlen", v, s, ipd, S * N, vo, so, S, H, D, code, mi.MI_F16,
                  st) for v, s in cop]
+        need = mi.merge_states_workspace_bytes(S, N, H, D)
+        ws = torch.empty(max(need // 4, 1), dtype=torch.float32, device="cuda")
+        w = [Raw(mi, "mi_merge_states_two_level", v, s, vo, so, S, N, H, D, code, mi.MI_F16, ws,
+                 need, st) for v, s in cop]
         ta = _median_us(torch, lambda i: a[i % 4](), iters)
         tb = _median_us(torch, lambda i: b[i % 4](), iters)
-        out.append(f"| merge_states {dt}->f16 | S={S} N={N} H={H} D={D} | {ta:.1f} | {tb:.1f} |")
+        tw = _median_us(torch, lambda i: w[i % 4](), iters)
+        out.append(f"| merge_states {dt}->f16 | S={S} N={N} H={H} D={D} | {ta:.1f} | {tb:.1f} | "
+                   f"{tw:.1f} |")
         del cop
         torch.cuda.empty_cache()
 

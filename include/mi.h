@@ -87,6 +87,27 @@ mi_status mi_merge_states(const void* v, const float* s, void* v_out, float* s_o
                           void* stream);
 
 /*
+ * N-state merge over two levels, for few positions with many states each (the
+ * many-index-set case of "F2 hints", section 7): each position's N states are
+ * cut into slices merged in parallel into fp32 partial states (level 1), then
+ * the partials are merged (level 2, the section-4 merge again). Same inputs,
+ * outputs and rules as mi_merge_states; results equal up to rounding order.
+ *   workspace : fp32 device buffer of at least the bytes reported by
+ *               mi_merge_states_workspace (may be NULL when that is 0, in
+ *               which case this is one launch of mi_merge_states); it must not
+ *               overlap any other argument. Two launches on `stream`.
+ */
+mi_status mi_merge_states_two_level(const void* v, const float* s, void* v_out, float* s_out,
+                                    int64_t S, int32_t N, int32_t H, int32_t D,
+                                    mi_dtype v_dtype, mi_dtype out_dtype, float* workspace,
+                                    size_t ws_bytes, void* stream);
+
+/* Workspace bytes mi_merge_states_two_level needs for this shape (0: one level
+ * suffices). Host only. */
+mi_status mi_merge_states_workspace(int64_t S, int32_t N, int32_t H, int32_t D,
+                                    size_t* ws_bytes);
+
+/*
  * Two-state merge in place with an optional per-position mask (the
  * merge_state_in_place variant named in "F2 hints: merge_state, base-2 LSE
  * merge", section 7; section 3 for the merge itself).

@@ -44,6 +44,9 @@ SIGNATURES = {
                             ctypes.c_int, _P, ctypes.c_size_t, _P, _P, ctypes.c_int, _P],
     "mi_prefix_attention_workspace": [_I32, _I32, _I32, _I32, _I32, _P],
     "mi_merge_state_in_place": [_P, _P, _P, _P, _P, _I64, _I32, _I32, ctypes.c_int, _P],
+    "mi_merge_states_two_level": [_P, _P, _P, _P, _I64, _I32, _I32, _I32, ctypes.c_int,
+                                  ctypes.c_int, _P, ctypes.c_size_t, _P],
+    "mi_merge_states_workspace": [_I64, _I32, _I32, _I32, _P],
     "mi_merge_sink": [_P, _P, _P, _P, _P, _I64, _I32, _I32, ctypes.c_int, ctypes.c_int, _P],
     "mi_merge_states_varlen": [_P, _P, _P, _I64, _P, _P, _I64, _I32, _I32, ctypes.c_int,
                                ctypes.c_int, _P],
@@ -151,6 +154,35 @@ def merge_states(v, s, out_dtype=None, v_out=None, s_out=None, return_s=True):
         s_out = torch.empty((S, H), dtype=torch.float32, device=v.device)
     _call("mi_merge_states", _ptr(v), _ptr(s), _ptr(v_out), _ptr(s_out), S, N, H, D, _dt(v),
           _dt(v_out), _stream(v))
+    return v_out, s_out
+
+
+def merge_states_workspace_bytes(S: int, N: int, H: int, D: int) -> int:
+    out = ctypes.c_size_t()
+    _call("mi_merge_states_workspace", S, N, H, D, ctypes.byref(out))
+    return out.value
+
+
+def merge_states_two_level(v, s, out_dtype=None, v_out=None, s_out=None, workspace=None,
+                           return_s=True):
+    """N-state merge over two levels (few positions, many states):
+    v [S, N, H, D], s [S, N, H] -> (v [S, H, D], s [S, H])."""
+    _check_cuda(v, s, v_out, s_out, workspace)
+    _f32(s, "s"), _f32(s_out, "s_out"), _f32(workspace, "workspace")
+    if v.dim() != 4 or s.shape != v.shape[:3]:
+        raise ValueError("merge_states_two_level: v must be [S, N, H, D] and s [S, N, H]")
+    S, N, H, D = v.shape
+    out_dtype = out_dtype or (v_out.dtype if v_out is not None else v.dtype)
+    if v_out is None:
+        v_out = torch.empty((S, H, D), dtype=out_dtype, device=v.device)
+    if s_out is None and return_s:
+        s_out = torch.empty((S, H), dtype=torch.float32, device=v.device)
+    need = merge_states_workspace_bytes(S, N, H, D)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=v.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * 4
+    _call("mi_merge_states_two_level", _ptr(v), _ptr(s), _ptr(v_out), _ptr(s_out), S, N, H, D,
+          _dt(v), _dt(v_out), _ptr(workspace), ws_bytes, _stream(v))
     return v_out, s_out
 
 

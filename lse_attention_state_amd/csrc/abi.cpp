@@ -322,6 +322,49 @@ mi_status mi_split_kv_decode_fused(const void* q, const void* k_cache, const voi
                                               out_dtype));
 }
 
+mi_status mi_merge_states_workspace(int64_t S, int32_t N, int32_t H, int32_t D,
+                                   size_t* ws_bytes) {
+  if (!ws_bytes) return MI_ERR_NULL;
+  if (S < 0 || N <= 0 || H <= 0 || D <= 0) return MI_ERR_SHAPE;
+  const int parts = mi::merge_states_parts(S, N, H);
+  *ws_bytes = parts == 1 ? 0 : static_cast<size_t>(S) * parts * H * (D + 1) * sizeof(float);
+  return MI_OK;
+}
+
+mi_status mi_merge_states_two_level(const void* v, const float* s, void* v_out, float* s_out,
+                                    int64_t S, int32_t N, int32_t H, int32_t D,
+                                    mi_dtype v_dtype, mi_dtype out_dtype, float* workspace,
+                                    size_t ws_bytes, void* stream) {
+  if (!v || !s || !v_out) return MI_ERR_NULL;
+  if (S < 0 || N <= 0) return MI_ERR_SHAPE;
+  mi_status st = check_merge_dims(H, D, v_dtype, out_dtype);
+  if (st != MI_OK) return st;
+  if (!size_ok(S, N, H, static_cast<int64_t>(D) * 4)) return MI_ERR_SHAPE;
+  size_t need = 0;
+  st = mi_merge_states_workspace(S, N, H, D, &need);
+  if (st != MI_OK) return st;
+  if (need > 0 && !workspace) return MI_ERR_NULL;
+  if (ws_bytes < need) return MI_ERR_SHAPE;
+  if (!aligned(v, 16) || !aligned(v_out, 16) || !aligned(s, 4) || !aligned(s_out, 4) ||
+      !aligned(workspace, 16))
+    return MI_ERR_UNSUPPORTED;
+  const int64_t in_v = S * N * H * D * dtype_bytes(v_dtype);
+  const int64_t in_s = S * N * H * 4;
+  const int64_t out_v = S * H * D * dtype_bytes(out_dtype);
+  const int64_t out_s = S * H * 4;
+  const int64_t ws_b = static_cast<int64_t>(need);
+  if (overlaps(v_out, out_v, v, in_v) || overlaps(v_out, out_v, s, in_s) ||
+      overlaps(s_out, out_s, v, in_v) || overlaps(s_out, out_s, s, in_s) ||
+      overlaps(s_out, out_s, v_out, out_v) || overlaps(workspace, ws_b, v, in_v) ||
+      overlaps(workspace, ws_b, s, in_s) || overlaps(workspace, ws_b, v_out, out_v) ||
+      overlaps(workspace, ws_b, s_out, out_s))
+    return MI_ERR_ALIAS;
+  if (S == 0) return MI_OK;
+  return from_hip(mi::launch_merge_states_two_level(v, s, v_out, s_out, S, N, H, D, v_dtype,
+                                                    out_dtype, workspace,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
 mi_status mi_merge_state_in_place(void* v, float* s, const void* v_other, const float* s_other,
                                   const uint8_t* mask, int64_t S, int32_t H, int32_t D,
                                   mi_dtype v_dtype, void* stream) {

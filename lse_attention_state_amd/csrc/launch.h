@@ -23,9 +23,18 @@ hipError_t launch_merge_sink(const void* v, const float* s, const float* sink, v
                              hipStream_t stream);
 
 // Segments [indptr[p], indptr[p+1]) of v [total, H, D]; indptr null: N states per position.
+// parts > 1 (indptr null): each position's states cut into `parts` slices,
+// written as [S, parts, H, D] partial states (a two-level merge's first level).
 hipError_t launch_merge_segments(const void* v, const float* s, const int32_t* indptr,
                                  int64_t total, int N, void* vo, float* so, int64_t S, int H,
-                                 int D, int dt_in, int dt_out, hipStream_t stream);
+                                 int D, int dt_in, int dt_out, hipStream_t stream, int parts = 1);
+
+// Two-level N-state merge: the number of slices per position (1 = one level),
+// and the merge itself with an fp32 workspace of S * parts * H * (D + 1) floats.
+int merge_states_parts(int64_t S, int N, int H);
+hipError_t launch_merge_states_two_level(const void* v, const float* s, void* vo, float* so,
+                                         int64_t S, int N, int H, int D, int dt_in, int dt_out,
+                                         float* ws, hipStream_t stream);
 
 hipError_t launch_split_kv_partial(const void* q, const void* kc, const void* vc,
                                    const int32_t* page_table, int pt_stride,

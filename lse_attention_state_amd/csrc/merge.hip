@@ -238,11 +238,14 @@ hipError_t merge_state_mode(const void* va, const float* sa, const void* vb, con
 // unit), 1024 for teams of more than four waves.
 constexpr int kSegMaxD = 512;
 
+// parts > 1 (no indptr): each position's N states are cut into `parts`
+// consecutive slices of ceil(N / parts), and row (pos * parts + part) * H + h
+// merges one slice -- the first level of a two-level merge.
 template <int DTI, int DTO, int K, int kSegThreads>
 __global__ __launch_bounds__(kSegThreads) void merge_segments_kernel(
     const void* __restrict__ v, const float* __restrict__ s, const int32_t* __restrict__ indptr,
     int64_t total, int N, void* __restrict__ vo, float* __restrict__ so, int64_t rows, int H,
-    int D, int lanes_shift, int team_shift) {
+    int D, int lanes_shift, int team_shift, int parts) {
   __shared__ float lds_acc[kSegThreads / 64][kSegMaxD];
   __shared__ float lds_mz[kSegThreads / 64][2];
   const int L = 1 << lanes_shift;
@@ -256,18 +259,25 @@ __global__ __launch_bounds__(kSegThreads) void merge_segments_kernel(
   const bool row_ok = row < rows;
   const int d0 = c * 8;
   const bool lane_ok = d0 < D;
-  const int64_t pos = row_ok ? row / H : 0;
-  const int h = row_ok ? static_cast<int>(row - pos * H) : 0;
+  const int64_t ph = row_ok ? row / H : 0;   // position (and slice)
+  const int h = row_ok ? static_cast<int>(row - ph * H) : 0;
   int64_t start = 0, end = 0;
   if (row_ok) {
     if (indptr != nullptr) {
-      start = indptr[pos];
-      end = indptr[pos + 1];
+      start = indptr[ph];
+      end = indptr[ph + 1];
       start = start < 0 ? 0 : (start > total ? total : start);
       end = end < start ? start : (end > total ? total : end);
-    } else {
-      start = pos * N;
+    } else if (parts == 1) {
+      start = ph * N;
       end = start + N;
+    } else {
+      const int64_t pos = ph / parts;
+      const int64_t per = (N + parts - 1) / parts;
+      const int64_t last = pos * N + N;
+      start = pos * N + (ph - pos * parts) * per;
+      start = start < last ? start : last;
+      end = start + per < last ? start + per : last;
     }
   }
   const int64_t n = end - start;
@@ -364,19 +374,20 @@ __global__ __launch_bounds__(kSegThreads) void merge_segments_kernel(
 template <int DTI, int DTO, int kThr>
 hipError_t merge_segments_kt(int K, dim3 grid, hipStream_t st, const void* v, const float* s,
                              const int32_t* indptr, int64_t total, int N, void* vo, float* so,
-                             int64_t rows, int H, int D, int lanes_shift, int team_shift) {
+                             int64_t rows, int H, int D, int lanes_shift, int team_shift,
+                             int parts) {
   switch (K) {
     case 1:
-      merge_segments_kernel<DTI, DTO, 1, kThr><<<grid, kThr, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
+      merge_segments_kernel<DTI, DTO, 1, kThr><<<grid, kThr, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts);
       break;
     case 2:
-      merge_segments_kernel<DTI, DTO, 2, kThr><<<grid, kThr, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
+      merge_segments_kernel<DTI, DTO, 2, kThr><<<grid, kThr, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts);
       break;
     case 4:
-      merge_segments_kernel<DTI, DTO, 4, kThr><<<grid, kThr, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
+      merge_segments_kernel<DTI, DTO, 4, kThr><<<grid, kThr, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts);
       break;
     default:
-      merge_segments_kernel<DTI, DTO, 8, kThr><<<grid, kThr, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
+      merge_segments_kernel<DTI, DTO, 8, kThr><<<grid, kThr, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts);
       break;
   }
   return hipGetLastError();
@@ -386,26 +397,27 @@ hipError_t merge_segments_kt(int K, dim3 grid, hipStream_t st, const void* v, co
 template <int DTI, int DTO>
 hipError_t merge_segments_k(int K, int64_t rows, hipStream_t st, const void* v, const float* s,
                             const int32_t* indptr, int64_t total, int N, void* vo, float* so,
-                            int H, int D, int lanes_shift, int team_shift) {
+                            int H, int D, int lanes_shift, int team_shift, int parts) {
   const int threads = team_shift > 8 ? 1024 : 256;
   const int64_t rows_per_block = threads >> team_shift;
   const dim3 grid(static_cast<unsigned>((rows + rows_per_block - 1) / rows_per_block));
   if (threads == 1024)
-    return merge_segments_kt<DTI, DTO, 1024>(K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
-  return merge_segments_kt<DTI, DTO, 256>(K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift);
+    return merge_segments_kt<DTI, DTO, 1024>(K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts);
+  return merge_segments_kt<DTI, DTO, 256>(K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts);
 }
 
 template <int DTI>
 hipError_t merge_segments_out(int dt_out, int K, int64_t rows, hipStream_t st, const void* v,
                               const float* s, const int32_t* indptr, int64_t total, int N,
-                              void* vo, float* so, int H, int D, int lanes_shift, int team_shift) {
+                              void* vo, float* so, int H, int D, int lanes_shift, int team_shift,
+                              int parts) {
   switch (dt_out) {
     case MI_F16:
-      return merge_segments_k<DTI, MI_F16>(K, rows, st, v, s, indptr, total, N, vo, so, H, D, lanes_shift, team_shift);
+      return merge_segments_k<DTI, MI_F16>(K, rows, st, v, s, indptr, total, N, vo, so, H, D, lanes_shift, team_shift, parts);
     case MI_BF16:
-      return merge_segments_k<DTI, MI_BF16>(K, rows, st, v, s, indptr, total, N, vo, so, H, D, lanes_shift, team_shift);
+      return merge_segments_k<DTI, MI_BF16>(K, rows, st, v, s, indptr, total, N, vo, so, H, D, lanes_shift, team_shift, parts);
     default:
-      return merge_segments_k<DTI, MI_F32>(K, rows, st, v, s, indptr, total, N, vo, so, H, D, lanes_shift, team_shift);
+      return merge_segments_k<DTI, MI_F32>(K, rows, st, v, s, indptr, total, N, vo, so, H, D, lanes_shift, team_shift, parts);
   }
 }
 
@@ -472,15 +484,16 @@ hipError_t launch_merge_sink(const void* v, const float* s, const float* sink, v
 
 hipError_t launch_merge_segments(const void* v, const float* s, const int32_t* indptr,
                                  int64_t total, int N, void* vo, float* so, int64_t S, int H,
-                                 int D, int dt_in, int dt_out, hipStream_t st) {
-  const int64_t rows = S * H;
+                                 int D, int dt_in, int dt_out, hipStream_t st, int parts) {
+  const int64_t rows = S * parts * H;
   const int L = next_pow2(D / 8);
   const int lanes_shift = log2_int(L);
   // Team size from the average set size: up to 8 states in flight per lane;
   // more lane groups when sets are longer, and more still (while each group
   // keeps at least one state) when there are too few rows to give the device
   // about 16 waves per compute unit.
-  const int64_t avg = indptr != nullptr ? (S > 0 ? (total + S - 1) / S : 0) : N;
+  const int64_t avg = indptr != nullptr ? (S > 0 ? (total + S - 1) / S : 0)
+                                        : (static_cast<int64_t>(N) + parts - 1) / parts;
   constexpr int64_t kTargetLanes = 4096 * 64;
   const int max_groups = 1024 / L;
   int G = 1;
@@ -490,10 +503,37 @@ hipError_t launch_merge_segments(const void* v, const float* s, const int32_t* i
   const int64_t per_lane = (avg + G - 1) / G;
   const int K = per_lane >= 8 ? 8 : next_pow2(static_cast<int>(per_lane > 0 ? per_lane : 1));
   switch (dt_in) {
-    case MI_F16: return merge_segments_out<MI_F16>(dt_out, K, rows, st, v, s, indptr, total, N, vo, so, H, D, lanes_shift, team_shift);
-    case MI_BF16: return merge_segments_out<MI_BF16>(dt_out, K, rows, st, v, s, indptr, total, N, vo, so, H, D, lanes_shift, team_shift);
-    default: return merge_segments_out<MI_F32>(dt_out, K, rows, st, v, s, indptr, total, N, vo, so, H, D, lanes_shift, team_shift);
+    case MI_F16: return merge_segments_out<MI_F16>(dt_out, K, rows, st, v, s, indptr, total, N, vo, so, H, D, lanes_shift, team_shift, parts);
+    case MI_BF16: return merge_segments_out<MI_BF16>(dt_out, K, rows, st, v, s, indptr, total, N, vo, so, H, D, lanes_shift, team_shift, parts);
+    default: return merge_segments_out<MI_F32>(dt_out, K, rows, st, v, s, indptr, total, N, vo, so, H, D, lanes_shift, team_shift, parts);
   }
+}
+
+int merge_states_parts(int64_t S, int N, int H) {
+  // Two levels only when rows alone give the device few workgroups: cut each
+  // row's states into slices of at least 64 until there are about 2048 rows.
+  // (Measured on MI355X: slices of at least 64 states and about 2048 rows beat
+  // 32 or 16 states and 4096 or 8192 rows.)
+  const int64_t rows = S * H;
+  int parts = 1;
+  while (parts < 64 && rows * parts < 2048 && N / (2 * parts) >= 64) parts *= 2;
+  return parts;
+}
+
+hipError_t launch_merge_states_two_level(const void* v, const float* s, void* vo, float* so,
+                                         int64_t S, int N, int H, int D, int dt_in, int dt_out,
+                                         float* ws, hipStream_t st) {
+  const int parts = merge_states_parts(S, N, H);
+  if (parts == 1) return launch_merge_states(v, s, vo, so, S, N, H, D, dt_in, dt_out, st);
+  // Level 1: slice states -> fp32 partial states [S, parts, H, D] and [S, parts, H].
+  float* wv = ws;
+  float* wsl = ws + S * parts * H * D;
+  hipError_t e = launch_merge_segments(v, s, nullptr, S * N, N, wv, wsl, S, H, D, dt_in, MI_F32,
+                                       st, parts);
+  if (e != hipSuccess) return e;
+  // Level 2: the N-state merge of the partials ([S, parts, H, D] is that layout).
+  return launch_merge_segments(wv, wsl, nullptr, S * parts, parts, vo, so, S, H, D, MI_F32,
+                               dt_out, st, 1);
 }
 
 hipError_t launch_merge_states(const void* v, const float* s, void* vo, float* so, int64_t S,
@@ -504,7 +544,7 @@ hipError_t launch_merge_states(const void* v, const float* s, void* vo, float* s
   // S*H = 32, N = 64 fp32 in 8.4 us against 11.6; S*H = 1024, N = 16 in 8.1
   // against 8.8); with many rows the N-state kernel's lighter merge wins.
   if (rows < 2048 && N >= 8)
-    return launch_merge_segments(v, s, nullptr, S * N, N, vo, so, S, H, D, dt_in, dt_out, st);
+    return launch_merge_segments(v, s, nullptr, S * N, N, vo, so, S, H, D, dt_in, dt_out, st, 1);
   const int L = next_pow2(D / 8);
   const int lanes_shift = log2_int(L);
   // Split the N states of a row over G lane groups when rows alone would not

@@ -141,3 +141,29 @@ def test_split_kv_decode_varlen_validation():
     assert _vdec(cnt=P((7 << 30) + 64)) == EALIAS  # counters inside o
     assert _vdec(op=P((1 << 30) + 64)) == EALIAS   # o_part inside the K cache
     assert _vdec(B=0, total=0) == OK
+
+
+def test_merge_states_workspace_and_two_level_validation():
+    lib = mi.lib()
+    out = ctypes.c_size_t()
+    assert lib.mi_merge_states_workspace(64, 1024, 1, 128, None) == ENULL
+    assert lib.mi_merge_states_workspace(-1, 4, 1, 128, ctypes.byref(out)) == ESHAPE
+    assert lib.mi_merge_states_workspace(64, 1024, 1, 128, ctypes.byref(out)) == OK
+    assert out.value == 64 * 16 * 1 * 129 * 4          # 16 slices of 64 states per position
+    assert lib.mi_merge_states_workspace(65536, 4, 8, 128, ctypes.byref(out)) == OK
+    assert out.value == 0                                # many rows: one level
+
+    def call(**kw):
+        a = dict(v=P(0), s=P(1 << 30), vo=P(2 << 30), so=P(3 << 30), S=64, N=1024, H=1, D=128,
+                 dti=F32, dto=F16, ws=P(4 << 30), wsb=64 * 16 * 129 * 4)
+        a.update(kw)
+        return lib.mi_merge_states_two_level(a["v"], a["s"], a["vo"], a["so"], a["S"], a["N"],
+                                             a["H"], a["D"], a["dti"], a["dto"], a["ws"],
+                                             ctypes.c_size_t(a["wsb"]), NULL)
+    assert call(ws=NULL) == ENULL                       # needed and missing
+    assert call(wsb=100) == ESHAPE                      # too small
+    assert call(ws=P((4 << 30) + 4)) == EUNSUP          # misaligned
+    assert call(ws=P(64)) == EALIAS                     # workspace inside the states
+    assert call(ws=P((2 << 30) + 16)) == EALIAS         # workspace over the output
+    assert call(N=0) == ESHAPE
+    assert call(S=0) == OK

@@ -331,3 +331,21 @@ def test_varlen_decode_many_sequences(fused, B):
     indptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     _say("total splits", int(indptr[-1]))
     _check_varlen(case, indptr, fused)
+
+
+@pytest.mark.parametrize("S,N,H,dt", [(64, 1024, 1, "f32"), (4, 3000, 2, "f16"), (1, 5000, 1, "bf16"),
+                                      (32, 64, 1, "f32"), (8, 200, 3, "f32")])
+def test_merge_states_two_level(S, N, H, dt):
+    """Few positions with many states, merged over two levels through an fp32
+    workspace; checked against the oracle's N-state merge."""
+    _say("two-level merge", S, N, H, dt)
+    c = inputs.merge_states_case(150 + N, S=S, N=N, H=H, D=128, dtype=dt, s_lo=-40, s_hi=40)
+    need = mi.merge_states_workspace_bytes(S, N, H, 128)
+    ws = (torch.full((max(need // 4, 1),), float("nan"), dtype=torch.float32, device="cuda")
+          if need else None)
+    vo, so = mi.merge_states_two_level(to_device(c["v"], dt), torch.from_numpy(c["s"]).cuda(),
+                                       out_dtype=torch.float16, workspace=ws)
+    torch.cuda.synchronize()
+    rv, rs = oracle.merge_states(c["v"], c["s"], dt)
+    check_values(vo, rv)
+    check_lse(so, rs)
