@@ -428,6 +428,31 @@ def sweep(torch, mi, inputs, iters, with_cpu=True):
     ones = torch.ones(32768, dtype=torch.uint8, device="cuda")
     out += ["", "| kernel | shape | µs | algorithmic bytes | GB/s | % of 8 TB/s |",
             "|---|---|---:|---:|---:|---:|"]
+    # The two core merges back to back (inputs rotated), for comparison with
+    # their once-per-step times in the default run.
+    msv = [(to_dev(ms["va"], "bf16", torch), torch.from_numpy(ms["sa"]).cuda(),
+            to_dev(ms["vb"], "bf16", torch), torch.from_numpy(ms["sb"]).cuda()) for _ in range(2)]
+    mvo, mso = torch.empty_like(msv[0][0]), torch.empty_like(msv[0][1])
+    calls = [Raw(mi, "mi_merge_state", a, b, c_, d, mvo, mso, rows_, 1, 128, mi.MI_BF16,
+                 mi.MI_BF16, st) for a, b, c_, d in msv]
+    t = _median_us(torch, lambda i: calls[i % 2](), iters)
+    by = rows_ * (3 * 256 + 3 * 4)
+    out.append(f"| merge_state, back to back | bf16 S=32768 H=32 D=128 | {t:.1f} | {by} | "
+               f"{by / (t * 1e-6) / 1e9:.0f} | {by / (t * 1e-6) / 8e12 * 100:.1f} |")
+    del msv, mvo, mso, calls
+    mss = inputs.merge_states_case(1001, S=65536, N=4, H=8, D=128, dtype="f16")
+    mv = [to_dev(mss["v"], "f16", torch) for _ in range(2)]
+    msd = torch.from_numpy(mss["s"]).cuda()
+    mvo = torch.empty((65536, 8, 128), dtype=torch.float16, device="cuda")
+    mso = torch.empty((65536, 8), dtype=torch.float32, device="cuda")
+    calls = [Raw(mi, "mi_merge_states", v_, msd, mvo, mso, 65536, 4, 8, 128, mi.MI_F16,
+                 mi.MI_F16, st) for v_ in mv]
+    t = _median_us(torch, lambda i: calls[i % 2](), iters)
+    by = 65536 * 8 * (4 * 128 * 2 + 4 * 4 + 128 * 2 + 4)
+    out.append(f"| merge_states, back to back | f16 S=65536 N=4 H=8 D=128 | {t:.1f} | {by} | "
+               f"{by / (t * 1e-6) / 1e9:.0f} | {by / (t * 1e-6) / 8e12 * 100:.1f} |")
+    del mv, mvo, mso, calls
+    torch.cuda.empty_cache()
     sink_calls = [Raw(mi, "mi_merge_sink", va[i], sa[i], sink, va[i], sa[i], 32768, 32, 128,
                       mi.MI_BF16, mi.MI_BF16, st) for i in range(2)]
     t = _median_us(torch, lambda i: sink_calls[i % 2](), iters)
