@@ -179,6 +179,15 @@ def test_varlen_plan_examples():
     # reach 1024 >= 340 items; the largest such c gives ceil(256/c) = 6 splits.
     c, counts = oracle.plan_splits_varlen(8, 8, np.full(8, 4096), 16, 170)
     assert (c, set(counts)) == (51, {6})
+    # empty sequences still cost one work item each (their outputs are written):
+    # 299 empty + one of 2048 pages, Hkv = 1, target 512 -> 299 + ceil(2048/c) >= 512
+    # holds up to c = 9 (228 splits), not c = 10 (205).
+    c, counts = oracle.plan_splits_varlen(300, 1, np.array([0] * 299 + [32768]), 16, 256)
+    assert c == 9 and counts[-1] == 228 and set(counts[:-1]) == {1}
+    # a batch too small to reach the target bottoms out at 8 pages per split:
+    # 100 pages -> 13 splits.
+    c, counts = oracle.plan_splits_varlen(1, 1, np.array([1600]), 16, 256)
+    assert (c, list(counts)) == (8, [13])
     # equal lengths reduce to the largest c that the uniform rule's target allows
     for B, n in ((1, 2048), (8, 256), (3, 1000)):
         c, counts = oracle.plan_splits_varlen(B, 8, np.full(B, n * 16), 16, 256)
