@@ -236,3 +236,22 @@ def test_fused_matches_two_launch_decode():
     assert torch.equal(a[3].view(torch.int32), b[3].view(torch.int32))
     assert torch.allclose(a[0], b[0], rtol=1e-5, atol=1e-6)
     assert torch.allclose(a[1], b[1], rtol=0, atol=1e-5)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_decode_maximum_split_count(fused):
+    """1024 splits (the largest supported): a 16385-token sequence gets one or
+    two pages per split and empty splits at the end; a short one is almost all
+    empty splits. Partials and outputs checked in full."""
+    _say("decode 1024 splits", fused)
+    ctx = np.array([16385, 33], np.int32)
+    case = inputs.paged_kv_case(61, ctx, 8, 2, 128, 16, dtype="bf16")
+    if fused:
+        out, lse, o_part, lse_part = _decode_fused(case, 1024)
+    else:
+        out, lse, o_part, lse_part = _decode(case, 1024)
+    o, s, op, sp = _oracle(case, 1024)
+    check_values(o_part, op, "o_part")
+    check_lse(lse_part, sp, "lse_part")
+    check_values(out, o, "o")
+    check_lse(lse, s, "lse")
