@@ -8,8 +8,8 @@ A step runs, on synthetic data resident in HBM:
                    planner picks the split count (64), then pass 1 and the
                    combine in one launch (mi_split_kv_decode_fused)
   4. cascade bf16: 64 requests share an 8192-token prefix (matrix-core level),
-                   each has a 512-token suffix (split-KV decode), then the two
-                   levels are merged with merge_state
+                   each has a 512-token suffix (split-KV decode) whose combine also
+                   merges the prefix chunk states (mi_cascade_decode, two launches)
 Inputs are rotated across copies so that consecutive uses of one buffer are
 separated by far more traffic than the 256 MB Infinity Cache holds.
 
@@ -260,19 +260,26 @@ def build_workload(torch, mi, inputs):
     merge_bytes = 2 * rows_s * 129 * 4 + rows_s * (128 * 2 + 4)
     prefix_flops = 4 * R * cHq * cas["prefix_len"] * 128
 
-    parts.append(dict(name="cascade_prefix", kernel="prefix_attention_kernel", bytes=prefix_bytes,
-                      flops=prefix_flops, run=lambda i: prefix_call(),
-                      shape=(f"bf16 64 requests x shared prefix 8192, Hq=32 Hkv=8 D=128, MFMA, "
-                             f"{n_ch} chunks + chunk merge")))
-    parts.append(dict(name="cascade_suffix", kernel="split_kv_partial_kernel", bytes=suffix_bytes,
-                      run=lambda i: suffix_call(),
-                      shape=f"bf16 64 requests x suffix 512, splits={c_splits}, single launch"))
-    parts.append(dict(name="cascade_merge", kernel="merge_state_kernel", bytes=merge_bytes,
-                      run=lambda i: level_merge(),
-                      shape="f32 prefix and suffix states [64, 32, 128] -> bf16"))
-
+    # The cascade in the step: mi_cascade_decode, two launches (the prefix
+    # chunk states, then the suffix decode whose combine also merges them).
+    f_o = torch.empty((R, cHq, 128), dtype=torch.bfloat16, device="cuda")
+    f_lse = torch.empty((R, cHq), dtype=torch.float32, device="cuda")
+    f_cnt = torch.zeros((R, cHkv), dtype=torch.int32, device="cuda")
+    cascade_call = Raw(mi, "mi_cascade_decode", cq, ck, cv, cpages, cas["prefix_len"], ctab,
+                       ctab.shape[1], clen, R, cHq, cHkv, 128, 16, cP, c_splits, cscale,
+                       mi.MI_BF16, c_ws, ws_bytes, c_op, c_lp, f_cnt, f_o, f_lse, mi.MI_BF16, st)
+    cascade_bytes = (cas["prefix_len"] * cHkv * 128 * 2 * 2 + R * 512 * cHkv * 128 * 2 * 2
+                     + 2 * cq.numel() * 2 + cpages.numel() * 4 + ctab.numel() * 4 + R * 4
+                     + 2 * rows_s * n_ch * 129 * 4 + 2 * rows_s * c_splits * 129 * 4
+                     + rows_s * (128 * 2 + 4))
+    parts.append(dict(name="cascade", kernel="prefix_attention_kernel", bytes=cascade_bytes,
+                      flops=prefix_flops, run=lambda i: cascade_call(),
+                      shape=(f"bf16 64 requests x (8192 shared + 512 own), Hq=32 Hkv=8 D=128: "
+                             f"prefix level on MFMA ({n_ch} chunks), suffix decode "
+                             f"(splits={c_splits}) whose combine merges the prefix chunks")))
     host = dict(ms=ms, mss=mss, dec=dec, splits=splits, decode_calls=decode_calls,
                 prefix_call=prefix_call, prefix_flops=prefix_flops, prefix_bytes=prefix_bytes,
+                four_launch=[prefix_call, suffix_call, level_merge],
                 fused_calls=fused_calls, partial_calls=partial_calls, combine_call=combine_call,
                 plan=plan)
     return parts, host
@@ -588,23 +595,31 @@ def main():
         step(i, True)
     torch.cuda.synchronize()
 
-    # Decode end to end, back to back with rotated K/V copies: single launch,
-    # and the two-launch form (pass 1, then the combine).
-    for label, calls in (("decode", host["fused_calls"]), ("decode_two_launch", host["decode_calls"])):
-        for i in range(args.steps):
-            host["plan"](i)
-            timer.start(label)
-            calls[i % 4]()
-            timer.stop(label)
+    # Back-to-back loops timed with one event pair around the whole loop (mean
+    # per call), so the GPU never waits for the host between launches.
+    def loop_us(fn, n):
+        fn(0)
         torch.cuda.synchronize()
-    for i in range(args.steps):
-        timer.start("split_kv_partial")
-        host["partial_calls"][i % 4]()
-        timer.stop("split_kv_partial")
-        timer.start("combine")
-        host["combine_call"]()
-        timer.stop("combine")
-    torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(n):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return 1000.0 * a.elapsed_time(b) / n
+
+    host["plan"](0)
+    extra = {
+        # decode end to end with rotated K/V copies: single launch, two launches
+        "decode": loop_us(lambda i: host["fused_calls"][i % 4](), args.steps),
+        "decode_two_launch": loop_us(lambda i: host["decode_calls"][i % 4](), args.steps),
+        "split_kv_partial": loop_us(lambda i: host["partial_calls"][i % 4](), args.steps),
+        "combine": loop_us(lambda i: host["combine_call"](), args.steps),
+        # the cascade's prefix level alone (MFMA contraction + chunk merge), and
+        # the cascade as four launches (prefix, chunk merge, suffix, level merge)
+        "cascade_prefix_level": loop_us(lambda i: host["prefix_call"](), args.steps),
+        "cascade_four_launch": loop_us(lambda i: [c_() for c_ in host["four_launch"]], args.steps),
+    }
 
     step_bytes = sum(p["bytes"] for p in parts)
     value = step_bytes / (ms_per_step / 1000.0) / 1e9
@@ -622,7 +637,7 @@ def main():
     traffic = counter_traffic(dom["kernel"])
     roofline = {"bound": "hbm", "achieved": dom["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": dom["frac"], "traffic": traffic, "kernel": dom["kernel"]}
-    decode_us = timer.mean_us("decode")
+    decode_us = extra["decode"]
     dec_bytes = [p for p in parts if p["name"] == "split_kv_decode"][0]["bytes"]
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -638,9 +653,12 @@ def main():
         "gpu_ms_per_step": round(gpu_ms_per_step, 4),
         "decode_us": round(decode_us, 2),
         "decode_GBs": round(dec_bytes / (decode_us * 1e-6) / 1e9, 1),
-        "decode_two_launch_us": round(timer.mean_us("decode_two_launch"), 2),
-        "decode_pass1_us": round(timer.mean_us("split_kv_partial"), 2),
-        "decode_combine_us": round(timer.mean_us("combine"), 2),
+        "decode_two_launch_us": round(extra["decode_two_launch"], 2),
+        "decode_pass1_us": round(extra["split_kv_partial"], 2),
+        "decode_combine_us": round(extra["combine"], 2),
+        "cascade_prefix_level_us": round(extra["cascade_prefix_level"], 2),
+        "cascade_prefix_level_TFLOPs": round(host["prefix_flops"] / (extra["cascade_prefix_level"] * 1e-6) / 1e12, 1),
+        "cascade_four_launch_us": round(extra["cascade_four_launch"], 2),
         "kernels": per,
         "roofline": roofline,
     }

@@ -321,6 +321,39 @@ mi_status mi_prefix_attention(const void* q, const void* k_cache, const void* v_
                               float* workspace, size_t ws_bytes, void* v_out, float* s_out,
                               mi_dtype out_dtype, void* stream);
 
+/*
+ * Two-level cascade decode in two launches ("F2 hints: merge_state, base-2 LSE
+ * merge", section 6; "L3 hints", sections 1-3): R requests share one prefix
+ * (read once, on the matrix cores, as in mi_prefix_attention) and each has its
+ * own suffix pages (split-KV decode as in mi_split_kv_decode_fused). The
+ * suffix decode's combine merges each row's suffix splits together with that
+ * row's prefix chunk states, so no separate merge launch follows.
+ *   q               : [R, Hq, D] of kv_dtype
+ *   k_cache,
+ *   v_cache         : [num_phys_pages, Hkv, page_size, D] of kv_dtype (one pool
+ *                     for prefix and suffix pages)
+ *   prefix_pages    : [ceil(prefix_len / page_size)] int32 (device)
+ *   suffix_table    : [R, suffix_stride] int32, suffix_lens : [R] int32 (device)
+ *   workspace       : fp32 device buffer of at least mi_prefix_attention_workspace
+ *                     bytes (prefix chunk states)
+ *   o_part, lse_part: [R, Hq, suffix_splits, D] / [R, Hq, suffix_splits] fp32
+ *   counters        : [R, Hkv] int32, all zero before the first call, left zero
+ *   o               : [R, Hq, D] of out_dtype;  lse : [R, Hq] fp32 base 2 (may be NULL)
+ * The result is attention over prefix followed by suffix for every (request,
+ * query head). Supported sizes, clamping of device data and the rules for
+ * counters as in mi_split_kv_decode_fused; calls sharing counters must not run
+ * concurrently.
+ */
+mi_status mi_cascade_decode(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* prefix_pages, int32_t prefix_len,
+                            const int32_t* suffix_table, int32_t suffix_stride,
+                            const int32_t* suffix_lens, int32_t R, int32_t Hq, int32_t Hkv,
+                            int32_t D, int32_t page_size, int64_t num_phys_pages,
+                            int32_t suffix_splits, float sm_scale, mi_dtype kv_dtype,
+                            float* workspace, size_t ws_bytes, float* o_part, float* lse_part,
+                            int32_t* counters, void* o, float* lse, mi_dtype out_dtype,
+                            void* stream);
+
 /* Workspace bytes mi_prefix_attention needs for this shape (host only). */
 mi_status mi_prefix_attention_workspace(int32_t R, int32_t Hq, int32_t Hkv, int32_t D,
                                         int32_t prefix_len, size_t* ws_bytes);

@@ -43,6 +43,9 @@ SIGNATURES = {
     "mi_prefix_attention": [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I64, _F,
                             ctypes.c_int, _P, ctypes.c_size_t, _P, _P, ctypes.c_int, _P],
     "mi_prefix_attention_workspace": [_I32, _I32, _I32, _I32, _I32, _P],
+    "mi_cascade_decode": [_P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I64,
+                          _I32, _F, ctypes.c_int, _P, ctypes.c_size_t, _P, _P, _P, _P, _P,
+                          ctypes.c_int, _P],
     "mi_merge_state_in_place": [_P, _P, _P, _P, _P, _I64, _I32, _I32, ctypes.c_int, _P],
     "mi_merge_states_two_level": [_P, _P, _P, _P, _I64, _I32, _I32, _I32, ctypes.c_int,
                                   ctypes.c_int, _P, ctypes.c_size_t, _P],
@@ -451,3 +454,41 @@ def cascade_decode(q, k_cache, v_cache, prefix_pages, prefix_len: int, suffix_ta
                                    sm_scale, out_dtype=torch.float32)
     o, lse = merge_state(vp, sp, vs, ss, out_dtype=out_dtype)
     return o, lse, (vp, sp), (vs, ss)
+
+
+def cascade_decode_fused(q, k_cache, v_cache, prefix_pages, prefix_len: int, suffix_table,
+                         suffix_lens, sm_scale: float, suffix_splits: int = 1, out_dtype=None,
+                         workspace=None, o_part=None, lse_part=None, counters=None, out=None,
+                         lse=None, return_lse=True):
+    """Two-level cascade decode in two launches (prefix level on the matrix cores,
+    then the suffix decode whose combine also merges the prefix chunk states)
+    -> (o [R, Hq, D], lse [R, Hq])."""
+    _check_cuda(q, k_cache, v_cache, prefix_pages, suffix_table, suffix_lens)
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q must be [R, Hq, D] and k/v caches [pages, Hkv, PAGE, D]")
+    if prefix_pages.dtype != torch.int32 or suffix_table.dtype != torch.int32 or \
+            suffix_lens.dtype != torch.int32:
+        raise TypeError("page lists, tables and lengths must be int32")
+    R, Hq, D = q.shape
+    P, Hkv, page, _ = k_cache.shape
+    out_dtype = out_dtype or (out.dtype if out is not None else q.dtype)
+    need = prefix_attention_workspace_bytes(R, Hq, Hkv, D, prefix_len)
+    if workspace is None:
+        workspace = torch.empty(max(need // 4, 1), dtype=torch.float32, device=q.device)
+    if o_part is None:
+        o_part = torch.empty((R, Hq, suffix_splits, D), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((R, Hq, suffix_splits), dtype=torch.float32, device=q.device)
+    if counters is None:
+        counters = torch.zeros((R, Hkv), dtype=torch.int32, device=q.device)
+    if out is None:
+        out = torch.empty((R, Hq, D), dtype=out_dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((R, Hq), dtype=torch.float32, device=q.device)
+    _check_cuda(workspace, o_part, lse_part, counters, out, lse)
+    _call("mi_cascade_decode", _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(prefix_pages),
+          prefix_len, _ptr(suffix_table), suffix_table.shape[1], _ptr(suffix_lens), R, Hq, Hkv,
+          D, page, P, suffix_splits, float(sm_scale), _dt(q), _ptr(workspace),
+          workspace.numel() * 4, _ptr(o_part), _ptr(lse_part), _ptr(counters), _ptr(out),
+          _ptr(lse), _dt(out), _stream(q))
+    return out, lse

@@ -595,4 +595,52 @@ mi_status mi_prefix_attention(const void* q, const void* k_cache, const void* v_
                                               static_cast<hipStream_t>(stream)));
 }
 
+mi_status mi_cascade_decode(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* prefix_pages, int32_t prefix_len,
+                            const int32_t* suffix_table, int32_t suffix_stride,
+                            const int32_t* suffix_lens, int32_t R, int32_t Hq, int32_t Hkv,
+                            int32_t D, int32_t page_size, int64_t num_phys_pages,
+                            int32_t suffix_splits, float sm_scale, mi_dtype kv_dtype,
+                            float* workspace, size_t ws_bytes, float* o_part, float* lse_part,
+                            int32_t* counters, void* o, float* lse, mi_dtype out_dtype,
+                            void* stream) {
+  if (!o || !counters || !workspace) return MI_ERR_NULL;
+  if (prefix_len > 0 && !prefix_pages) return MI_ERR_NULL;
+  if (prefix_len < 0) return MI_ERR_SHAPE;
+  DecodeShape shp;
+  mi_status st = check_decode(q, k_cache, v_cache, suffix_table, suffix_stride, suffix_lens, R,
+                              Hq, Hkv, D, page_size, num_phys_pages, suffix_splits, kv_dtype,
+                              o_part, lse_part, &shp);
+  if (st != MI_OK) return st;
+  st = check_decode_outputs(q, k_cache, v_cache, suffix_table, suffix_lens, o_part, lse_part,
+                            counters, true, o, lse, R, Hq, Hkv, D, out_dtype, shp);
+  if (st != MI_OK) return st;
+  size_t need = 0;
+  st = mi_prefix_attention_workspace(R, Hq, Hkv, D, prefix_len, &need);
+  if (st != MI_OK) return st;
+  if (ws_bytes < need) return MI_ERR_SHAPE;
+  if (!aligned(workspace, 16) || !aligned(prefix_pages, 4)) return MI_ERR_UNSUPPORTED;
+  const int64_t ws_b = static_cast<int64_t>(need);
+  const int64_t pp_b = int64_t(mi::ceil_div(prefix_len, page_size)) * 4;
+  const int64_t o_b = int64_t(R) * Hq * D * dtype_bytes(out_dtype);
+  const void* all[10] = {q, k_cache, v_cache, suffix_table, suffix_lens, o_part, lse_part,
+                         counters, o, lse};
+  const int64_t all_b[10] = {shp.q_bytes, shp.cache_bytes, shp.cache_bytes, shp.pt_bytes,
+                             shp.ctx_bytes, shp.opart_bytes, shp.lpart_bytes,
+                             int64_t(R) * Hkv * 4, o_b, int64_t(R) * Hq * 4};
+  for (int i = 0; i < 10; ++i)
+    if (overlaps(workspace, ws_b, all[i], all_b[i]) || overlaps(prefix_pages, pp_b, all[i], all_b[i]))
+      return MI_ERR_ALIAS;
+  if (overlaps(workspace, ws_b, prefix_pages, pp_b)) return MI_ERR_ALIAS;
+  if (R == 0) return MI_OK;
+  int n_chunks, chunk_tokens;
+  mi::prefix_attention_plan(R, Hq, Hkv, prefix_len, &n_chunks, &chunk_tokens);
+  float* ws_o = workspace;
+  float* ws_s = workspace + static_cast<int64_t>(R) * Hq * n_chunks * D;
+  return from_hip(mi::launch_cascade_decode(
+      q, k_cache, v_cache, prefix_pages, prefix_len, suffix_table, suffix_stride, suffix_lens, R,
+      Hq, Hkv, num_phys_pages, suffix_splits, sm_scale, kv_dtype, ws_o, ws_s, o_part, lse_part,
+      counters, o, lse, out_dtype, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -371,11 +371,10 @@ void prefix_attention_plan(int R, int Hq, int Hkv, int prefix_len, int* n_chunks
   *n_chunks = prefix_len > 0 ? (prefix_len + tokens - 1) / tokens : 1;
 }
 
-hipError_t launch_prefix_attention(const void* q, const void* kc, const void* vc,
-                                   const int32_t* prefix_pages, int prefix_len, int R, int Hq,
-                                   int Hkv, int64_t num_phys, float sm_scale, int kv_dtype,
-                                   float* ws_o, float* ws_s, void* v_out, float* s_out,
-                                   int out_dtype, hipStream_t st) {
+hipError_t launch_prefix_chunks(const void* q, const void* kc, const void* vc,
+                                const int32_t* prefix_pages, int prefix_len, int R, int Hq,
+                                int Hkv, int64_t num_phys, float sm_scale, int kv_dtype,
+                                float* ws_o, float* ws_s, hipStream_t st) {
   int n_chunks, chunk_tokens;
   prefix_attention_plan(R, Hq, Hkv, prefix_len, &n_chunks, &chunk_tokens);
   const int G = Hq / Hkv;
@@ -394,11 +393,41 @@ hipError_t launch_prefix_attention(const void* q, const void* kc, const void* vc
     prefix_attention_kernel<MI_F16><<<grid, kThreads, 0, st>>>(
         q16, k16, v16, prefix_pages, prefix_len, n_rows, Hq, Hkv, G, num_phys, chunk_tokens,
         n_chunks, scale, ws_o, ws_s);
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_prefix_attention(const void* q, const void* kc, const void* vc,
+                                   const int32_t* prefix_pages, int prefix_len, int R, int Hq,
+                                   int Hkv, int64_t num_phys, float sm_scale, int kv_dtype,
+                                   float* ws_o, float* ws_s, void* v_out, float* s_out,
+                                   int out_dtype, hipStream_t st) {
+  hipError_t e = launch_prefix_chunks(q, kc, vc, prefix_pages, prefix_len, R, Hq, Hkv, num_phys,
+                                      sm_scale, kv_dtype, ws_o, ws_s, st);
   if (e != hipSuccess) return e;
+  int n_chunks, chunk_tokens;
+  prefix_attention_plan(R, Hq, Hkv, prefix_len, &n_chunks, &chunk_tokens);
   // Merge the chunk states: ws [R*Hq, n_chunks, 1, D] -> [R*Hq, 1, D].
   return launch_merge_states(ws_o, ws_s, v_out, s_out, static_cast<int64_t>(R) * Hq, n_chunks,
                              1, kD, MI_F32, out_dtype, st);
+}
+
+hipError_t launch_cascade_decode(const void* q, const void* kc, const void* vc,
+                                 const int32_t* prefix_pages, int prefix_len,
+                                 const int32_t* suffix_table, int suffix_stride,
+                                 const int32_t* suffix_lens, int R, int Hq, int Hkv,
+                                 int64_t num_phys, int suffix_splits, float sm_scale,
+                                 int kv_dtype, float* ws_o, float* ws_s, float* o_part,
+                                 float* lse_part, int32_t* counters, void* o, float* lse,
+                                 int out_dtype, hipStream_t st) {
+  hipError_t e = launch_prefix_chunks(q, kc, vc, prefix_pages, prefix_len, R, Hq, Hkv, num_phys,
+                                      sm_scale, kv_dtype, ws_o, ws_s, st);
+  if (e != hipSuccess) return e;
+  int n_chunks, chunk_tokens;
+  prefix_attention_plan(R, Hq, Hkv, prefix_len, &n_chunks, &chunk_tokens);
+  // The suffix level, whose combine also merges each row's prefix chunk states.
+  return launch_split_kv_partial(q, kc, vc, suffix_table, suffix_stride, suffix_lens, R, Hq, Hkv,
+                                 num_phys, suffix_splits, sm_scale, kv_dtype, o_part, lse_part,
+                                 st, counters, o, lse, out_dtype, ws_o, ws_s, n_chunks);
 }
 
 }  // namespace mi

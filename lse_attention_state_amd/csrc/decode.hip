@@ -89,35 +89,41 @@ __device__ __forceinline__ void unpack8(const u32x4_t& w, float (&x)[8]) {
 
 // The combine of one (sequence, query head) row by one wave: merge the
 // `count` partial states of that row ("L3 hints: split-KV decode and LSE
-// merge", section 3) into o[row, :] (dtype DTO) and lse[row] (base 2,
-// optional). Split j's state is lse_part[first + j * stride] and
-// o_part[(first + j * stride) * D, ...]: stride 1 for the uniform layout
-// [B, Hq, splits], Hq for the per-sequence layout [total, Hq]. Lane l owns the
-// 8-element chunk (l%16)*8 of D for the splits j = l/16 (mod 4); each pass
-// keeps 8 of its splits' loads in flight, then the four split sub-groups are
-// merged across lanes.
+// merge", section 3), and `prior_n` earlier states of the row if given, into
+// o[row, :] (dtype DTO) and lse[row] (base 2, optional). Split j's state is
+// lse_part[first + j * stride] and o_part[(first + j * stride) * D, ...]:
+// stride 1 for the uniform layout [B, Hq, splits], Hq for the per-sequence
+// layout [total, Hq]. Earlier state i is prior_s[row * prior_n + i] and
+// prior_o[(row * prior_n + i) * D, ...] (a cascade's prefix chunk states).
+// Lane l owns the 8-element chunk (l%16)*8 of D for the states j = l/16
+// (mod 4); each pass keeps 8 of its states' loads in flight, then the four
+// sub-groups are merged across lanes.
 template <int DTO>
 __device__ void combine_row(const float* o_part, const float* lse_part, int64_t first,
-                            int64_t stride, int count, int64_t row, void* o, float* lse,
+                            int64_t stride, int count, const float* prior_o,
+                            const float* prior_s, int prior_n, int64_t row, void* o, float* lse,
                             int lane) {
   const int c = lane & 15;
   const int sg = lane >> 4;
+  const int n_all = prior_n + count;
   float m = -kInf, z = 0.0f, acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-  for (int k0 = sg; k0 < count; k0 += 32) {
+  for (int k0 = sg; k0 < n_all; k0 += 32) {
     float sv[8], x[8][8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int k = k0 + 4 * u;
-      const int64_t r = first + static_cast<int64_t>(k < count ? k : 0) * stride;
-      sv[u] = lse_part[r];
-      load8<MI_F32>(o_part, r * kD + c * 8, x[u]);
+      int k = k0 + 4 * u;
+      k = k < n_all ? k : 0;
+      const bool pre = k < prior_n;
+      const int64_t r = pre ? row * prior_n + k : first + static_cast<int64_t>(k - prior_n) * stride;
+      sv[u] = (pre ? prior_s : lse_part)[r];
+      load8<MI_F32>(pre ? prior_o : o_part, r * kD + c * 8, x[u]);
     }
     float cm = m;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      sv[u] = k0 + 4 * u < count ? sanitize_lse(sv[u]) : -kInf;
+      sv[u] = k0 + 4 * u < n_all ? sanitize_lse(sv[u]) : -kInf;
       cm = __builtin_fmaxf(cm, sv[u]);
     }
     const float keep = guarded_exp2(m - cm);
@@ -201,6 +207,9 @@ __device__ __forceinline__ void find_segment(const int32_t* indptr, int B, int i
 // many), and the partials are laid out [total items, Hq, D] / [total, Hq].
 // Otherwise blockIdx.y is the split and blockIdx.z the sequence, and the
 // partials are [B, Hq, num_splits, D] / [B, Hq, num_splits].
+// prior_n > 0 (fused form only): the combine also merges prior_n earlier
+// states per (sequence, query head) row, prior_o [rows, prior_n, D] and
+// prior_s [rows, prior_n] -- the shared-prefix states of a cascade.
 template <int DT, int G, int DTO, bool kVar>
 __global__ __launch_bounds__(kThreads) void split_kv_partial_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
@@ -208,7 +217,8 @@ __global__ __launch_bounds__(kThreads) void split_kv_partial_kernel(
     const int32_t* __restrict__ ctx_lens, int Hkv, int64_t num_phys, int num_splits,
     float qk_scale_log2, float* __restrict__ o_part, float* __restrict__ lse_part,
     int32_t* __restrict__ counters, void* __restrict__ o, float* __restrict__ lse,
-    const int32_t* __restrict__ split_indptr, int B) {
+    const int32_t* __restrict__ split_indptr, int B, const float* __restrict__ prior_o,
+    const float* __restrict__ prior_s, int prior_n) {
   __shared__ float lds_acc[kWaves][G][kD];
   __shared__ float lds_ml[kWaves][G][2];
 
@@ -451,7 +461,7 @@ __global__ __launch_bounds__(kThreads) void split_kv_partial_kernel(
     const float2 res = make_float2(o0 * inv, o1 * inv);
     const float lse_val = (Z > 0.0f) ? M + hw_log2(Z) : -kInf;
     if constexpr (DTO >= 0) {
-      if (nsplit == 1) {
+      if (nsplit == 1 && prior_n == 0) {
         // One split: the combine is the identity, so write the result directly.
         *reinterpret_cast<float2*>(out) = res;
         if (lane == 0) lse_part[prow] = lse_val;
@@ -477,7 +487,24 @@ __global__ __launch_bounds__(kThreads) void split_kv_partial_kernel(
   }
 
   if constexpr (DTO >= 0) {
-    if (nsplit == 1) return;  // written directly above
+    if (nsplit == 1 && prior_n == 0) return;  // written directly above
+    if (nsplit == 1) {
+      // The only split, with earlier states to merge: this workgroup holds
+      // everything it needs, so ordering its own stores before its own loads
+      // (workgroup scope) suffices -- no counter, and no device-wide acquire
+      // that would drop other workgroups' cached K/V.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      for (int h = wave; h < G; h += kWaves) {
+        const int64_t row = static_cast<int64_t>(b) * Hq + hkv * G + h;
+        const int64_t first = kVar ? static_cast<int64_t>(seg_first) * Hq + hkv * G + h
+                                   : row * num_splits;
+        combine_row<DTO>(o_part, lse_part, first, 1, 1, prior_o, prior_s, prior_n, row, o, lse,
+                         lane);
+      }
+      return;
+    }
     // Hand-off: every workgroup publishes its partials (agent-scope release)
     // and bumps the (sequence, kv head) counter; the one that brings it to
     // num_splits performs the acquire and merges all splits of its heads.
@@ -501,9 +528,10 @@ __global__ __launch_bounds__(kThreads) void split_kv_partial_kernel(
       const int64_t row = static_cast<int64_t>(b) * Hq + hkv * G + h;
       if constexpr (kVar)
         combine_row<DTO>(o_part, lse_part, static_cast<int64_t>(seg_first) * Hq + hkv * G + h, Hq,
-                         nsplit, row, o, lse, lane);
+                         nsplit, prior_o, prior_s, prior_n, row, o, lse, lane);
       else
-        combine_row<DTO>(o_part, lse_part, row * num_splits, 1, nsplit, row, o, lse, lane);
+        combine_row<DTO>(o_part, lse_part, row * num_splits, 1, nsplit, prior_o, prior_s,
+                         prior_n, row, o, lse, lane);
     }
     if (threadIdx.x == 0) counters[static_cast<int64_t>(b) * Hkv + hkv] = 0;
   }
@@ -514,14 +542,15 @@ hipError_t launch_group(int G, dim3 grid, hipStream_t st, const void* q, const v
                         const void* vc, const int32_t* pt, int pt_stride, const int32_t* ctx,
                         int Hkv, int64_t num_phys, int num_splits, float scale, float* o_part,
                         float* lse_part, int32_t* counters, void* o, float* lse,
-                        const int32_t* split_indptr, int B) {
+                        const int32_t* split_indptr, int B, const float* prior_o,
+                        const float* prior_s, int prior_n) {
   const uint16_t* q16 = static_cast<const uint16_t*>(q);
   const uint16_t* k16 = static_cast<const uint16_t*>(kc);
   const uint16_t* v16 = static_cast<const uint16_t*>(vc);
 #define MI_LAUNCH_G(GG)                                                                        \
   split_kv_partial_kernel<DT, GG, DTO, kVar><<<grid, kThreads, 0, st>>>(                       \
       q16, k16, v16, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part, \
-      counters, o, lse, split_indptr, B)
+      counters, o, lse, split_indptr, B, prior_o, prior_s, prior_n)
   switch (G) {
     case 1: MI_LAUNCH_G(1); break;
     case 2: MI_LAUNCH_G(2); break;
@@ -537,16 +566,17 @@ hipError_t launch_dtype(int out_dtype, int G, dim3 grid, hipStream_t st, const v
                         const void* kc, const void* vc, const int32_t* pt, int pt_stride,
                         const int32_t* ctx, int Hkv, int64_t num_phys, int num_splits, float scale,
                         float* o_part, float* lse_part, int32_t* counters, void* o, float* lse,
-                        const int32_t* split_indptr, int B) {
+                        const int32_t* split_indptr, int B, const float* prior_o = nullptr,
+                        const float* prior_s = nullptr, int prior_n = 0) {
   switch (out_dtype) {
     case MI_F16:
-      return launch_group<DT, MI_F16, kVar>(G, grid, st, q, kc, vc, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part, counters, o, lse, split_indptr, B);
+      return launch_group<DT, MI_F16, kVar>(G, grid, st, q, kc, vc, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part, counters, o, lse, split_indptr, B, prior_o, prior_s, prior_n);
     case MI_BF16:
-      return launch_group<DT, MI_BF16, kVar>(G, grid, st, q, kc, vc, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part, counters, o, lse, split_indptr, B);
+      return launch_group<DT, MI_BF16, kVar>(G, grid, st, q, kc, vc, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part, counters, o, lse, split_indptr, B, prior_o, prior_s, prior_n);
     case MI_F32:
-      return launch_group<DT, MI_F32, kVar>(G, grid, st, q, kc, vc, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part, counters, o, lse, split_indptr, B);
+      return launch_group<DT, MI_F32, kVar>(G, grid, st, q, kc, vc, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part, counters, o, lse, split_indptr, B, prior_o, prior_s, prior_n);
     default:
-      return launch_group<DT, -1, kVar>(G, grid, st, q, kc, vc, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part, nullptr, nullptr, nullptr, split_indptr, B);
+      return launch_group<DT, -1, kVar>(G, grid, st, q, kc, vc, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part, nullptr, nullptr, nullptr, split_indptr, B, nullptr, nullptr, 0);
   }
 }
 
@@ -558,7 +588,8 @@ hipError_t launch_split_kv_partial(const void* q, const void* kc, const void* vc
                                    int64_t num_phys_pages, int num_splits, float sm_scale,
                                    int kv_dtype, float* o_part, float* lse_part,
                                    hipStream_t st, int32_t* counters, void* o, float* lse,
-                                   int out_dtype) {
+                                   int out_dtype, const float* prior_o, const float* prior_s,
+                                   int prior_n) {
   const int G = Hq / Hkv;
   const dim3 grid(static_cast<unsigned>(Hkv), static_cast<unsigned>(num_splits),
                   static_cast<unsigned>(B));
@@ -569,10 +600,12 @@ hipError_t launch_split_kv_partial(const void* q, const void* kc, const void* vc
   if (kv_dtype == MI_F16)
     return launch_dtype<MI_F16, false>(dto, G, grid, st, q, kc, vc, page_table, pt_stride,
                                        ctx_lens, Hkv, num_phys_pages, num_splits, scale, o_part,
-                                       lse_part, counters, o, lse, nullptr, B);
+                                       lse_part, counters, o, lse, nullptr, B, prior_o, prior_s,
+                                       prior_n);
   return launch_dtype<MI_BF16, false>(dto, G, grid, st, q, kc, vc, page_table, pt_stride,
                                       ctx_lens, Hkv, num_phys_pages, num_splits, scale, o_part,
-                                      lse_part, counters, o, lse, nullptr, B);
+                                      lse_part, counters, o, lse, nullptr, B, prior_o, prior_s,
+                                      prior_n);
 }
 
 hipError_t launch_split_kv_partial_varlen(const void* q, const void* kc, const void* vc,

@@ -42,7 +42,9 @@ hipError_t launch_split_kv_partial(const void* q, const void* kc, const void* vc
                                    int64_t num_phys_pages, int num_splits, float sm_scale,
                                    int kv_dtype, float* o_part, float* lse_part,
                                    hipStream_t stream, int32_t* counters = nullptr,
-                                   void* o = nullptr, float* lse = nullptr, int out_dtype = -1);
+                                   void* o = nullptr, float* lse = nullptr, int out_dtype = -1,
+                                   const float* prior_o = nullptr, const float* prior_s = nullptr,
+                                   int prior_n = 0);
 
 // Per-sequence split counts (split_indptr [B+1] on the device). counters null:
 // pass 1 only; otherwise pass 1 fused with the combine.
@@ -57,6 +59,17 @@ hipError_t launch_split_kv_partial_varlen(const void* q, const void* kc, const v
 // Cascade prefix: chunk count and chunk length (tokens) for a shape.
 void prefix_attention_plan(int R, int Hq, int Hkv, int prefix_len, int* n_chunks,
                            int* chunk_tokens);
+
+// Cascade in two launches: the prefix chunk states into ws, then the suffix
+// decode (fused) whose combine merges the splits with those chunk states.
+hipError_t launch_cascade_decode(const void* q, const void* kc, const void* vc,
+                                 const int32_t* prefix_pages, int prefix_len,
+                                 const int32_t* suffix_table, int suffix_stride,
+                                 const int32_t* suffix_lens, int R, int Hq, int Hkv,
+                                 int64_t num_phys, int suffix_splits, float sm_scale,
+                                 int kv_dtype, float* ws_o, float* ws_s, float* o_part,
+                                 float* lse_part, int32_t* counters, void* o, float* lse,
+                                 int out_dtype, hipStream_t stream);
 
 hipError_t launch_prefix_attention(const void* q, const void* kc, const void* vc,
                                    const int32_t* prefix_pages, int prefix_len, int R, int Hq,

@@ -93,3 +93,57 @@ def test_cascade_64_requests_8k_prefix_512_suffix():
     check_values(vs, so_, "suffix v")
     check_lse(ss, ss_, "suffix s")
     _say("cascade stats", stats, "suffix splits", splits)
+
+
+def _fused(case, prefix_len, suffix_lens, splits, out_dtype=None):
+    q, k, v = _dev(case)
+    pages = torch.from_numpy(case["prefix_pages"]).cuda()
+    st = torch.from_numpy(case["suffix_table"]).cuda()
+    sl = torch.from_numpy(np.ascontiguousarray(suffix_lens, np.int32)).cuda()
+    R, Hq, Hkv = case["R"], case["Hq"], case["Hkv"]
+    nan = float("nan")
+    out = torch.full((R, Hq, 128), nan, dtype=out_dtype or q.dtype, device="cuda")
+    lse = torch.full((R, Hq), nan, dtype=torch.float32, device="cuda")
+    counters = torch.zeros((R, Hkv), dtype=torch.int32, device="cuda")
+    mi.cascade_decode_fused(q, k, v, pages, prefix_len, st, sl, case["sm_scale"],
+                            suffix_splits=splits, counters=counters, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert not counters.any(), "counters must be left zero"
+    return out, lse
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+def test_cascade_decode_fused_64_requests(splits):
+    """64 requests x (8192 shared + 512 own), two launches: equals unsplit
+    attention over prefix + suffix."""
+    _say("cascade fused full", splits)
+    case = inputs.cascade_case(1005)
+    o, lse = _fused(case, case["prefix_len"], case["suffix_lens"], splits)
+    ro, rs = oracle.attention(case["q"], case["k"], case["v"], case["full_table"],
+                              case["full_lens"], case["sm_scale"], "bf16", "bf16")
+    stats = check_values(o, ro)
+    check_lse(lse, rs)
+    _say("stats", stats)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("R,Hq,Hkv,prefix_len,splits", [(3, 8, 2, 100, 1), (5, 4, 1, 37, 3),
+                                                        (20, 16, 2, 530, 4), (7, 8, 8, 0, 2),
+                                                        (16, 32, 8, 1024, 1)])
+def test_cascade_decode_fused_ragged(dtype, R, Hq, Hkv, prefix_len, splits):
+    """Ragged prefix lengths (including none) and per-request suffix lengths
+    (including 0): the result is the merge of the prefix-only and suffix-only
+    oracle states (disjoint key sets merge exactly)."""
+    _say("cascade fused ragged", dtype, R, Hq, Hkv, prefix_len, splits)
+    case = inputs.cascade_case(950 + R + prefix_len, R=R, prefix_len=max(16, -(-prefix_len // 16) * 16),
+                               suffix_len=80, Hq=Hq, Hkv=Hkv, dtype=dtype)
+    suffix_lens = np.random.default_rng(951 + R).integers(0, 81, size=R).astype(np.int32)
+    suffix_lens[0] = 0
+    o, lse = _fused(case, prefix_len, suffix_lens, splits, out_dtype=torch.float32)
+    po, ps = _prefix_oracle(case, prefix_len)
+    so_, ss_ = oracle.attention(case["q"], case["k"], case["v"], case["suffix_table"],
+                                suffix_lens, case["sm_scale"], dtype, dtype)
+    ro, rs = oracle.merge_state(po.astype(np.float32), ps.astype(np.float32),
+                                so_.astype(np.float32), ss_.astype(np.float32), "f32")
+    check_values(o, ro)
+    check_lse(lse, rs)
