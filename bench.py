@@ -279,7 +279,7 @@ def build_workload(torch, mi, inputs):
                              f"(splits={c_splits}) whose combine merges the prefix chunks")))
     host = dict(ms=ms, mss=mss, dec=dec, splits=splits, decode_calls=decode_calls,
                 prefix_call=prefix_call, prefix_flops=prefix_flops, prefix_bytes=prefix_bytes,
-                four_launch=[prefix_call, suffix_call, level_merge],
+                four_launch=[prefix_call, suffix_call, level_merge], cascade_call=cascade_call,
                 fused_calls=fused_calls, partial_calls=partial_calls, combine_call=combine_call,
                 plan=plan)
     return parts, host
@@ -619,6 +619,7 @@ def main():
         # the cascade as four launches (prefix, chunk merge, suffix, level merge)
         "cascade_prefix_level": loop_us(lambda i: host["prefix_call"](), args.steps),
         "cascade_four_launch": loop_us(lambda i: [c_() for c_ in host["four_launch"]], args.steps),
+        "cascade": loop_us(lambda i: host["cascade_call"](), args.steps),
     }
 
     step_bytes = sum(p["bytes"] for p in parts)
@@ -659,6 +660,7 @@ def main():
         "cascade_prefix_level_us": round(extra["cascade_prefix_level"], 2),
         "cascade_prefix_level_TFLOPs": round(host["prefix_flops"] / (extra["cascade_prefix_level"] * 1e-6) / 1e12, 1),
         "cascade_four_launch_us": round(extra["cascade_four_launch"], 2),
+        "cascade_two_launch_us": round(extra["cascade"], 2),
         "kernels": per,
         "roofline": roofline,
     }
