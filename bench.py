@@ -47,6 +47,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--configs", action="store_true",
+                    help=("instead of the step: one JSON line per workload (the two merges, "
+                          "decode at B=1 and on the mixed batch, the cascade) with median / "
+                          "p10 / p90 times, GB/s, and the fp64 oracle timed and compared beside "
+                          "it"))
     ap.add_argument("--sweep", action="store_true",
                     help=("instead of the step: split-count sweep over the page's three decode "
                           "workloads and the mixed batch (uniform and per-sequence plans), "
@@ -537,6 +542,205 @@ def cpu_baseline_sweep(oracle, inputs, ms, sink, indptr, vs_case):
     return L
 
 
+def _times_us(torch, fn, iters, warmup=10):
+    """Per-call HIP-event durations (µs) on the current stream."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = []
+    for i in range(iters):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn(i)
+        b.record()
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    return np.array([1000.0 * a.elapsed_time(b) for a, b in ev])
+
+
+_MANT = {"f16": 10, "bf16": 7, "f32": 23}
+_MIN_EXP = {"f16": -14, "bf16": -126, "f32": -126}
+
+
+def _agreement(got, ref, out_dt, got_s=None, ref_s=None):
+    """GPU output against the oracle's: max abs / rel error, how many elements
+    pass the 2e-3 + 2e-3|ref| rule only by one ulp of the output type, NaNs,
+    and the largest LSE difference (-inf must match -inf)."""
+    got = np.asarray(got, np.float64)
+    err = np.abs(got - ref)
+    stated = 2e-3 + 2e-3 * np.abs(ref)
+    a = np.abs(ref)
+    e = np.maximum(np.floor(np.log2(np.where(a > 0, a, 1.0))), _MIN_EXP[out_dt])
+    ulp = np.exp2(e - _MANT[out_dt])
+    r = {"max_abs_err": float(err.max(initial=0.0)),
+         "max_rel_err": float((err / np.maximum(a, 1e-30)).max(initial=0.0)),
+         "outside_tolerance": int((err > np.maximum(stated, ulp)).sum()),
+         "pass_by_ulp_only": int(((err > stated) & (err <= ulp)).sum()),
+         "nan": int(np.isnan(got).sum())}
+    if got_s is not None:
+        gs = np.asarray(got_s, np.float64)
+        fin = ~np.isneginf(ref_s)
+        r["lse_inf_pattern_equal"] = bool(np.array_equal(np.isneginf(gs), ~fin))
+        r["max_lse_err"] = float(np.abs(gs[fin] - ref_s[fin]).max(initial=0.0))
+        r["lse_nan"] = int(np.isnan(gs).sum())
+    return r
+
+
+def configs_report(torch, mi, inputs, iters, with_cpu):
+    """One JSON line per workload ("configs"): GPU times over `iters` calls
+    (median, p10, p90), algorithmic GB/s, and -- the cpu_baseline leg -- the
+    fp64 oracle on the same inputs, timed, with its outputs compared."""
+    import ctypes
+    import platform
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    threads = len(os.sched_getaffinity(0))
+    cpu = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    oracle = None
+    if with_cpu:
+        import oracle
+
+    def emit(name, shape, seed, by, ts, extra, oracle_run=None):
+        med = float(np.median(ts))
+        line = {"config": name, "shape": shape, "seed": seed, "algorithmic_bytes": by,
+                "us_median": round(med, 2), "us_p10": round(float(np.percentile(ts, 10)), 2),
+                "us_p90": round(float(np.percentile(ts, 90)), 2),
+                "GB/s": round(by / (med * 1e-6) / 1e9, 1),
+                "frac_of_8TB/s": round(by / (med * 1e-6) / 8e12, 4)}
+        line.update(extra)
+        if oracle_run is not None:
+            t0 = time.perf_counter()
+            cmp = oracle_run()
+            line["oracle"] = {"seconds": round(time.perf_counter() - t0, 3), "threads": threads,
+                              "cpu": cpu, "vs_gpu": cmp}
+        print(json.dumps(line), flush=True)
+
+    # 1. merge_states fp16 S=64 N=4 H=8 D=128
+    c1 = inputs.merge_states_case(1001, S=64, N=4, H=8, D=128, dtype="f16")
+    v1, s1 = to_dev(c1["v"], "f16", torch), torch.from_numpy(c1["s"]).cuda()
+    vo1 = torch.empty((64, 8, 128), dtype=torch.float16, device="cuda")
+    so1 = torch.empty((64, 8), dtype=torch.float32, device="cuda")
+    call = Raw(mi, "mi_merge_states", v1, s1, vo1, so1, 64, 4, 8, 128, mi.MI_F16, mi.MI_F16, st)
+    ts = _times_us(torch, lambda i: call(), iters)
+    def cmp1():
+        rv, rs = oracle.merge_states(c1["v"], c1["s"], "f16", threads)
+        return _agreement(vo1.float().cpu().numpy(), rv, "f16", so1.cpu().numpy(), rs)
+    emit("merge_states", "f16 S=64 N=4 H=8 D=128 (10% empty states)", 1001,
+         64 * 8 * (4 * 256 + 16 + 256 + 4), ts, {}, cmp1 if oracle else None)
+
+    # 2. merge_state bf16 S=32768 H=32 D=128, inputs rotated over two copies
+    c2 = inputs.merge_state_case(1002, S=32768, H=32, D=128, dtype="bf16")
+    cp = [(to_dev(c2["va"], "bf16", torch), torch.from_numpy(c2["sa"]).cuda(),
+           to_dev(c2["vb"], "bf16", torch), torch.from_numpy(c2["sb"]).cuda()) for _ in range(2)]
+    vo2 = torch.empty_like(cp[0][0])
+    so2 = torch.empty_like(cp[0][1])
+    calls = [Raw(mi, "mi_merge_state", a, b, c_, d, vo2, so2, 32768 * 32, 1, 128, mi.MI_BF16,
+                 mi.MI_BF16, st) for a, b, c_, d in cp]
+    ts = _times_us(torch, lambda i: calls[i % 2](), iters)
+
+    def cmp2():
+        rv, rs = oracle.merge_state(c2["va"], c2["sa"], c2["vb"], c2["sb"], "bf16", threads)
+        return _agreement(vo2.float().cpu().numpy(), rv, "bf16", so2.cpu().numpy(), rs)
+    emit("merge_state", "bf16 S=32768 H=32 D=128 (1% of rows empty)", 1002,
+         32768 * 32 * (3 * 256 + 12), ts, {}, cmp2 if oracle else None)
+    del cp, calls, vo2, so2
+    torch.cuda.empty_cache()
+
+    def decode_case(name, seed, ctx, plan, per_sequence=False):
+        case = inputs.paged_kv_case(seed, ctx, 32, 8, 128, 16, dtype="f16")
+        B = len(ctx)
+        q = to_dev(case["q"], "f16", torch)
+        k0, v0 = to_dev(case["k"], "f16", torch), to_dev(case["v"], "f16", torch)
+        kv = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(3)]
+        pt = torch.from_numpy(case["page_table"]).cuda()
+        cl = torch.from_numpy(ctx).cuda()
+        P = case["k"].shape[0]
+        scale = float(case["sm_scale"])
+        o = torch.empty((B, 32, 128), dtype=torch.float16, device="cuda")
+        lse = torch.empty((B, 32), dtype=torch.float32, device="cuda")
+        cnt = torch.zeros((B, 8), dtype=torch.int32, device="cuda")
+        if per_sequence:
+            indptr = mi.plan_splits_varlen(ctx, 8, 16)
+            total = int(indptr[-1])
+            ipd = torch.from_numpy(indptr).cuda()
+            op = torch.empty((total, 32, 128), dtype=torch.float32, device="cuda")
+            lp = torch.empty((total, 32), dtype=torch.float32, device="cuda")
+            calls = [Raw(mi, "mi_split_kv_decode_varlen", q, k, v, pt, pt.shape[1], cl, B, 32, 8,
+                         128, 16, P, ipd, total, scale, mi.MI_F16, op, lp, cnt, o, lse, mi.MI_F16,
+                         st) for k, v in kv]
+            splits, parts_rows = f"per sequence, total {total}", total
+        else:
+            n = mi.plan_splits(ctx, 8, 16)
+            op = torch.empty((B, 32, n, 128), dtype=torch.float32, device="cuda")
+            lp = torch.empty((B, 32, n), dtype=torch.float32, device="cuda")
+            calls = [Raw(mi, "mi_split_kv_decode_fused", q, k, v, pt, pt.shape[1], cl, B, 32, 8,
+                         128, 16, P, n, scale, mi.MI_F16, op, lp, cnt, o, lse, mi.MI_F16, st)
+                     for k, v in kv]
+            splits, parts_rows = n, B * n
+        t0 = time.perf_counter()
+        for _ in range(100):
+            plan()
+        plan_us = (time.perf_counter() - t0) * 1e4      # host µs per plan (outside the events)
+        ts = _times_us(torch, lambda i: calls[i % 4](), iters)
+        by = (int(ctx.astype(np.int64).sum()) * 8 * 128 * 2 * 2 + q.numel() * 2
+              + pt.numel() * 4 + B * 4 + (2 * parts_rows * 32 * 129 * 4 if parts_rows > B else 0)
+              + B * 32 * (256 + 4))
+
+        def cmp():
+            ro, rs = oracle.attention(case["q"], case["k"], case["v"], case["page_table"], ctx,
+                                      case["sm_scale"], "f16", "f16", threads)
+            return _agreement(o.float().cpu().numpy(), ro, "f16", lse.cpu().numpy(), rs)
+        emit(name, f"f16 B={B} Hq=32 Hkv=8 D=128 PAGE=16, single launch", seed, by, ts,
+             {"num_splits": splits, "host_plan_us": round(plan_us, 2)}, cmp if oracle else None)
+
+    # 3. decode B=1 ctx=32768 (64 splits); 4. the mixed batch (uniform and per-sequence plans)
+    ctx3 = np.array([32768], np.int32)
+    decode_case("split_kv_decode_b1_32k", 1003, ctx3, lambda: mi.plan_splits(ctx3, 8, 16))
+    ctx4 = inputs.mixed_ctx_lens(1004, 32)
+    decode_case("split_kv_decode_mixed_b32", 1004, ctx4, lambda: mi.plan_splits(ctx4, 8, 16))
+    decode_case("split_kv_decode_mixed_b32_per_sequence", 1004, ctx4,
+                lambda: mi.plan_splits_varlen(ctx4, 8, 16), per_sequence=True)
+    torch.cuda.empty_cache()
+
+    # 5. cascade: 64 requests x (8192 shared + 512 own), two launches
+    cas = inputs.cascade_case(1005)
+    R, Hq, Hkv = cas["R"], cas["Hq"], cas["Hkv"]
+    cq = to_dev(cas["q"], "bf16", torch)
+    k0, v0 = to_dev(cas["k"], "bf16", torch), to_dev(cas["v"], "bf16", torch)
+    kv = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(3)]
+    pages = torch.from_numpy(cas["prefix_pages"]).cuda()
+    tab = torch.from_numpy(cas["suffix_table"]).cuda()
+    lens = torch.from_numpy(cas["suffix_lens"]).cuda()
+    n = mi.plan_splits(cas["suffix_lens"], Hkv, 16)
+    wsb = mi.prefix_attention_workspace_bytes(R, Hq, Hkv, 128, cas["prefix_len"])
+    ws = torch.empty(wsb // 4, dtype=torch.float32, device="cuda")
+    op = torch.empty((R, Hq, n, 128), dtype=torch.float32, device="cuda")
+    lp = torch.empty((R, Hq, n), dtype=torch.float32, device="cuda")
+    cnt = torch.zeros((R, Hkv), dtype=torch.int32, device="cuda")
+    o = torch.empty((R, Hq, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((R, Hq), dtype=torch.float32, device="cuda")
+    calls = [Raw(mi, "mi_cascade_decode", cq, k, v, pages, cas["prefix_len"], tab, tab.shape[1],
+                 lens, R, Hq, Hkv, 128, 16, cas["k"].shape[0], n, float(cas["sm_scale"]),
+                 mi.MI_BF16, ws, wsb, op, lp, cnt, o, lse, mi.MI_BF16, st) for k, v in kv]
+    ts = _times_us(torch, lambda i: calls[i % 4](), iters)
+    n_ch = wsb // (R * Hq * 129 * 4)
+    rows = R * Hq
+    by = (cas["prefix_len"] * Hkv * 128 * 2 * 2 + R * 512 * Hkv * 128 * 2 * 2 + 2 * cq.numel() * 2
+          + pages.numel() * 4 + tab.numel() * 4 + R * 4 + 2 * rows * n_ch * 129 * 4
+          + 2 * rows * n * 129 * 4 + rows * (256 + 4))
+
+    def cmp5():
+        ro, rs = oracle.attention(cas["q"], cas["k"], cas["v"], cas["full_table"], cas["full_lens"],
+                                  cas["sm_scale"], "bf16", "bf16", threads)
+        return _agreement(o.float().cpu().numpy(), ro, "bf16", lse.cpu().numpy(), rs)
+    emit("cascade", "bf16 64 x (8192 shared + 512 own) Hq=32 Hkv=8 D=128, two launches", 1005,
+         by, ts, {"prefix_chunks": n_ch, "suffix_splits": n}, cmp5 if oracle else None)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -556,6 +760,10 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 5}))
+        return
+
+    if args.configs:
+        configs_report(torch, mi, inputs, max(args.steps, 100), not args.no_cpu_baseline)
         return
 
     if args.sweep:
