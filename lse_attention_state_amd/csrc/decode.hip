@@ -210,7 +210,10 @@ __device__ __forceinline__ void find_segment(const int32_t* indptr, int B, int i
 // prior_n > 0 (fused form only): the combine also merges prior_n earlier
 // states per (sequence, query head) row, prior_o [rows, prior_n, D] and
 // prior_s [rows, prior_n] -- the shared-prefix states of a cascade.
-template <int DT, int G, int DTO, bool kVar>
+// kPR > 0 (fused, one split per sequence, G <= 4, at most kPR prior states):
+// each wave loads its head's prior states (two columns per lane) into
+// registers at the start, so the merge at the end needs no memory round trip.
+template <int DT, int G, int DTO, bool kVar, int kPR>
 __global__ __launch_bounds__(kThreads) void split_kv_partial_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ page_table, int pt_stride,
@@ -265,6 +268,20 @@ __global__ __launch_bounds__(kThreads) void split_kv_partial_kernel(
 #pragma unroll
   for (int h = 0; h < G; ++h)
     qw[h] = *reinterpret_cast<const u32x4_t*>(q + (static_cast<int64_t>(b) * Hq + hkv * G + h) * kD + d0);
+
+  constexpr int kPRg = G <= kWaves ? kPR : 0;  // one head per wave
+  float2 pri_o[kPRg > 0 ? kPRg : 1];
+  float pri_s[kPRg > 0 ? kPRg : 1];
+  if constexpr (kPRg > 0) {
+    const int hw = wave < G ? wave : 0;
+    const int64_t r0 = (static_cast<int64_t>(b) * Hq + hkv * G + hw) * prior_n;
+#pragma unroll
+    for (int i = 0; i < kPRg; ++i) {
+      const int64_t r = r0 + (i < prior_n ? i : 0);
+      pri_s[i] = prior_s[r];
+      pri_o[i] = *reinterpret_cast<const float2*>(prior_o + r * kD + 2 * lane);
+    }
+  }
 
   // m[h] is the reference max, mu[h] the value subtracted before exp2 (m, or
   // 0 while m is -inf), thr[h] = m + kRescaleSlack; mu and thr change only
@@ -460,6 +477,39 @@ __global__ __launch_bounds__(kThreads) void split_kv_partial_kernel(
     float* out = o_part + prow * kD + 2 * lane;
     const float2 res = make_float2(o0 * inv, o1 * inv);
     const float lse_val = (Z > 0.0f) ? M + hw_log2(Z) : -kInf;
+    if constexpr (DTO >= 0 && kPRg > 0) {
+      // The only split: merge with this row's prior states held in registers.
+      *reinterpret_cast<float2*>(out) = res;
+      if (lane == 0) lse_part[prow] = lse_val;
+      float ps[kPRg];
+      float mx = lse_val;
+#pragma unroll
+      for (int i = 0; i < kPRg; ++i) {
+        ps[i] = i < prior_n ? sanitize_lse(pri_s[i]) : -kInf;
+        mx = __builtin_fmaxf(mx, ps[i]);
+      }
+      const float w0 = guarded_exp2(lse_val - mx);
+      float z = w0;
+      float a0 = w0 > 0.0f ? w0 * res.x : 0.0f;
+      float a1 = w0 > 0.0f ? w0 * res.y : 0.0f;
+#pragma unroll
+      for (int i = 0; i < kPRg; ++i) {
+        const float w = guarded_exp2(ps[i] - mx);
+        z += w;
+        a0 = w > 0.0f ? __builtin_fmaf(w, pri_o[i].x, a0) : a0;
+        a1 = w > 0.0f ? __builtin_fmaf(w, pri_o[i].y, a1) : a1;
+      }
+      const float zi = guarded_inv(z);
+      const float2 fin = make_float2(a0 * zi, a1 * zi);
+      if constexpr (DTO == MI_F32) {
+        *reinterpret_cast<float2*>(static_cast<float*>(o) + row * kD + 2 * lane) = fin;
+      } else {
+        const uint32_t w2 = DTO == MI_F16 ? pack_f16(fin.x, fin.y) : pack_bf16(fin.x, fin.y);
+        *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(o) + row * kD + 2 * lane) = w2;
+      }
+      if (lse != nullptr && lane == 0) lse[row] = (z > 0.0f) ? mx + hw_log2(z) : -kInf;
+      continue;
+    }
     if constexpr (DTO >= 0) {
       if (nsplit == 1 && prior_n == 0) {
         // One split: the combine is the identity, so write the result directly.
@@ -487,7 +537,7 @@ __global__ __launch_bounds__(kThreads) void split_kv_partial_kernel(
   }
 
   if constexpr (DTO >= 0) {
-    if (nsplit == 1 && prior_n == 0) return;  // written directly above
+    if (kPRg > 0 || (nsplit == 1 && prior_n == 0)) return;  // written directly above
     if (nsplit == 1) {
       // The only split, with earlier states to merge: this workgroup holds
       // everything it needs, so ordering its own stores before its own loads
@@ -537,7 +587,7 @@ __global__ __launch_bounds__(kThreads) void split_kv_partial_kernel(
   }
 }
 
-template <int DT, int DTO, bool kVar>
+template <int DT, int DTO, bool kVar, int kPR = 0>
 hipError_t launch_group(int G, dim3 grid, hipStream_t st, const void* q, const void* kc,
                         const void* vc, const int32_t* pt, int pt_stride, const int32_t* ctx,
                         int Hkv, int64_t num_phys, int num_splits, float scale, float* o_part,
@@ -548,7 +598,7 @@ hipError_t launch_group(int G, dim3 grid, hipStream_t st, const void* q, const v
   const uint16_t* k16 = static_cast<const uint16_t*>(kc);
   const uint16_t* v16 = static_cast<const uint16_t*>(vc);
 #define MI_LAUNCH_G(GG)                                                                        \
-  split_kv_partial_kernel<DT, GG, DTO, kVar><<<grid, kThreads, 0, st>>>(                       \
+  split_kv_partial_kernel<DT, GG, DTO, kVar, kPR><<<grid, kThreads, 0, st>>>(                  \
       q16, k16, v16, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part, \
       counters, o, lse, split_indptr, B, prior_o, prior_s, prior_n)
   switch (G) {
@@ -568,6 +618,20 @@ hipError_t launch_dtype(int out_dtype, int G, dim3 grid, hipStream_t st, const v
                         float* o_part, float* lse_part, int32_t* counters, void* o, float* lse,
                         const int32_t* split_indptr, int B, const float* prior_o = nullptr,
                         const float* prior_s = nullptr, int prior_n = 0) {
+  // Prior states in registers: one split, at most 16 of them, one head per wave.
+  constexpr int kPR = 16;
+  if constexpr (!kVar) {
+    if (prior_n > 0 && prior_n <= kPR && num_splits == 1 && G <= 4 && out_dtype >= 0) {
+      switch (out_dtype) {
+        case MI_F16:
+          return launch_group<DT, MI_F16, false, kPR>(G, grid, st, q, kc, vc, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part, counters, o, lse, split_indptr, B, prior_o, prior_s, prior_n);
+        case MI_BF16:
+          return launch_group<DT, MI_BF16, false, kPR>(G, grid, st, q, kc, vc, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part, counters, o, lse, split_indptr, B, prior_o, prior_s, prior_n);
+        default:
+          return launch_group<DT, MI_F32, false, kPR>(G, grid, st, q, kc, vc, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part, counters, o, lse, split_indptr, B, prior_o, prior_s, prior_n);
+      }
+    }
+  }
   switch (out_dtype) {
     case MI_F16:
       return launch_group<DT, MI_F16, kVar>(G, grid, st, q, kc, vc, pt, pt_stride, ctx, Hkv, num_phys, num_splits, scale, o_part, lse_part, counters, o, lse, split_indptr, B, prior_o, prior_s, prior_n);
