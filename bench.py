@@ -275,7 +275,8 @@ def build_workload(torch, mi, inputs):
                        mi.MI_BF16, c_ws, ws_bytes, c_op, c_lp, f_cnt, f_o, f_lse, mi.MI_BF16, st)
     cascade_bytes = (cas["prefix_len"] * cHkv * 128 * 2 * 2 + R * 512 * cHkv * 128 * 2 * 2
                      + 2 * cq.numel() * 2 + cpages.numel() * 4 + ctab.numel() * 4 + R * 4
-                     + 2 * rows_s * n_ch * 129 * 4 + 2 * rows_s * c_splits * 129 * 4
+                     + 2 * rows_s * n_ch * 129 * 4
+                     + (2 if c_splits > 1 else 1) * rows_s * c_splits * 129 * 4
                      + rows_s * (128 * 2 + 4))
     parts.append(dict(name="cascade", kernel="prefix_attention_kernel", bytes=cascade_bytes,
                       flops=prefix_flops, run=lambda i: cascade_call(),
@@ -731,7 +732,7 @@ def configs_report(torch, mi, inputs, iters, with_cpu):
     rows = R * Hq
     by = (cas["prefix_len"] * Hkv * 128 * 2 * 2 + R * 512 * Hkv * 128 * 2 * 2 + 2 * cq.numel() * 2
           + pages.numel() * 4 + tab.numel() * 4 + R * 4 + 2 * rows * n_ch * 129 * 4
-          + 2 * rows * n * 129 * 4 + rows * (256 + 4))
+          + (2 if n > 1 else 1) * rows * n * 129 * 4 + rows * (256 + 4))
 
     def cmp5():
         ro, rs = oracle.attention(cas["q"], cas["k"], cas["v"], cas["full_table"], cas["full_lens"],
