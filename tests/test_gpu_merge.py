@@ -2,7 +2,7 @@
 
 Workloads: the two-state merge at bf16 S=32768, H=32, D=128 (1% of rows with
 both states empty), the N-state merge at fp16 S=64, N=4, H=8, D=128 (10% of
-states empty), and smaller cases spanning several workgroups with ragged tails,
+states empty) and at S=65536 (sampled), and smaller cases spanning several workgroups with ragged tails,
 every dtype pair and the special LSE values.
 """
 import numpy as np
@@ -156,6 +156,36 @@ def test_merge_states_config_shape_with_all_empty_rows_and_special_lse():
         check_values(vo, rv)
         check_lse(so, rs)
     assert host64(so)[3, 2] == -np.inf and np.all(host64(vo)[3, 2] == 0)
+
+
+def test_merge_states_streaming_size_sampled():
+    """fp16 S=65536, N=4, H=8, D=128 (the size that streams HBM, same inputs and
+    launch as the measured step): every all-empty row checked, 4096 sampled
+    (position, head) rows against the oracle, plus global no-NaN."""
+    _say("merge_states streaming size")
+    S, N, H, D = 65536, 4, 8, 128
+    case = inputs.merge_states_case(1001, S=S, N=N, H=H, D=D, dtype="f16")
+    vo = torch.full((S, H, D), float("nan"), dtype=torch.float16, device="cuda")
+    so = torch.full((S, H), float("nan"), dtype=torch.float32, device="cuda")
+    mi.merge_states(to_device(case["v"], "f16"), torch.from_numpy(case["s"]).cuda(),
+                    v_out=vo, s_out=so)
+    torch.cuda.synchronize()
+    vh, sh = vo.view(-1, D), so.view(-1)
+    assert not torch.isnan(vh).any() and not torch.isnan(sh).any()
+    g = np.random.default_rng(1)
+    rows = np.sort(g.choice(S * H, size=4096, replace=False))
+    pos, head = rows // H, rows % H
+    rv, rs = oracle.merge_states(case["v"][pos, :, head][:, :, None, :],
+                                 case["s"][pos, :, head][:, :, None], "f16")
+    idx = torch.from_numpy(rows).cuda()
+    stats = check_values(vh[idx], rv.reshape(-1, D))
+    check_lse(sh[idx], rs.reshape(-1))
+    # all-empty (position, head) rows give exactly (0, -inf)
+    empty = np.flatnonzero(np.all(np.isneginf(case["s"]), axis=1).reshape(-1))
+    if empty.size:
+        e_idx = torch.from_numpy(empty).cuda()
+        assert torch.all(sh[e_idx] == float("-inf")) and torch.all(vh[e_idx] == 0)
+    _say("merge_states streaming size stats", stats)
 
 
 def test_merge_states_matches_pairwise_merge_state():
