@@ -2,8 +2,8 @@
 
 Workloads: the two-state merge at bf16 S=32768, H=32, D=128 (1% of rows with
 both states empty), the N-state merge at fp16 S=64, N=4, H=8, D=128 (10% of
-states empty) and at S=65536 (sampled), and smaller cases spanning several workgroups with ragged tails,
-every dtype pair and the special LSE values.
+states empty) and at S=65536 (sampled), and smaller cases spanning several
+workgroups with ragged tails, every dtype pair and the special LSE values.
 """
 import numpy as np
 import pytest
