@@ -314,20 +314,20 @@ def cpu_baseline(host, oracle):
                        f"{dt:.2f} s wall; GB/s counts the same algorithmic bytes as the GPU")}
 
 
-def _median_us(torch, fn, iters, warmup=5):
-    """Median of per-call HIP-event durations (µs) on the current stream."""
+def _loop_us(torch, fn, iters, warmup=5):
+    """Mean time per call (µs) over `iters` calls enqueued back to back, with
+    one HIP event pair around the loop on the current stream (events between
+    calls would add their own gaps to kernels of a few microseconds)."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    ev = []
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
     for i in range(iters):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
         fn(i)
-        b.record()
-        ev.append((a, b))
+    b.record()
     torch.cuda.synchronize()
-    return float(np.median([1000.0 * a.elapsed_time(b) for a, b in ev]))
+    return 1000.0 * a.elapsed_time(b) / iters
 
 
 def sweep(torch, mi, inputs, iters, with_cpu=True):
@@ -340,8 +340,9 @@ def sweep(torch, mi, inputs, iters, with_cpu=True):
     Hq, Hkv, D, PAGE = 32, 8, 128, 16
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     out = ["# Split-count sweep and merge variants (fp16 decode, Hq=32, Hkv=8, D=128, PAGE=16)",
-           "", f"Device compute units: {cus}. Median of {iters} calls, HIP events, K/V rotated "
-           "over 4 copies. GB/s counts valid K/V tokens once plus the partials written and read.",
+           "", f"Device compute units: {cus}. Mean per call over {iters} calls enqueued back to "
+           "back (one HIP event pair around the loop), inputs rotated over copies (K/V over 4). "
+           "GB/s counts valid K/V tokens once plus the partials written and read.",
            ""]
     workloads = [("1 x 32768", np.array([32768], np.int32)),
                  ("8 x 4096", np.full(8, 4096, np.int32)),
@@ -373,8 +374,8 @@ def sweep(torch, mi, inputs, iters, with_cpu=True):
             one = [Raw(mi, "mi_split_kv_decode_fused", q, k, v, pt, pt.shape[1], ctxd, B, Hq, Hkv,
                        D, PAGE, P, n, scale, mi.MI_F16, op, lp, cnt, o, lse, mi.MI_F16, st)
                    for k, v in kv]
-            t2 = _median_us(torch, lambda i: two[i % 4](), iters)
-            t1 = _median_us(torch, lambda i: one[i % 4](), iters)
+            t2 = _loop_us(torch, lambda i: two[i % 4](), iters)
+            t1 = _loop_us(torch, lambda i: one[i % 4](), iters)
             part = B * Hq * n * (D + 1) * 4 * 2 if n > 1 else 0
             label = "uniform" + (" (planner's pick)" if n == pick else "")
             rows.append(f"| {name} | {label} | {n} | {t2:.1f} | {t1:.1f} | "
@@ -390,8 +391,8 @@ def sweep(torch, mi, inputs, iters, with_cpu=True):
         vone = [Raw(mi, "mi_split_kv_decode_varlen", q, k, v, pt, pt.shape[1], ctxd, B, Hq, Hkv, D,
                     PAGE, P, ipd, total, scale, mi.MI_F16, op, lp, cnt, o, lse, mi.MI_F16, st)
                 for k, v in kv]
-        t2 = _median_us(torch, lambda i: vtwo[i % 4](), iters)
-        t1 = _median_us(torch, lambda i: vone[i % 4](), iters)
+        t2 = _loop_us(torch, lambda i: vtwo[i % 4](), iters)
+        t1 = _loop_us(torch, lambda i: vone[i % 4](), iters)
         counts = np.diff(indptr)
         part = Hq * total * (D + 1) * 4 * 2 if total > B else 0
         rows.append(f"| {name} | per-sequence (counts {counts.min()}..{counts.max()}) | "
@@ -421,9 +422,9 @@ def sweep(torch, mi, inputs, iters, with_cpu=True):
         ws = torch.empty(max(need // 4, 1), dtype=torch.float32, device="cuda")
         w = [Raw(mi, "mi_merge_states_two_level", v, s, vo, so, S, N, H, D, code, mi.MI_F16, ws,
                  need, st) for v, s in cop]
-        ta = _median_us(torch, lambda i: a[i % 4](), iters)
-        tb = _median_us(torch, lambda i: b[i % 4](), iters)
-        tw = _median_us(torch, lambda i: w[i % 4](), iters)
+        ta = _loop_us(torch, lambda i: a[i % 4](), iters)
+        tb = _loop_us(torch, lambda i: b[i % 4](), iters)
+        tw = _loop_us(torch, lambda i: w[i % 4](), iters)
         out.append(f"| merge_states {dt}->f16 | S={S} N={N} H={H} D={D} | {ta:.1f} | {tb:.1f} | "
                    f"{tw:.1f} |")
         del cop
@@ -448,7 +449,7 @@ def sweep(torch, mi, inputs, iters, with_cpu=True):
     mvo, mso = torch.empty_like(msv[0][0]), torch.empty_like(msv[0][1])
     calls = [Raw(mi, "mi_merge_state", a, b, c_, d, mvo, mso, rows_, 1, 128, mi.MI_BF16,
                  mi.MI_BF16, st) for a, b, c_, d in msv]
-    t = _median_us(torch, lambda i: calls[i % 2](), iters)
+    t = _loop_us(torch, lambda i: calls[i % 2](), iters)
     by = rows_ * (3 * 256 + 3 * 4)
     out.append(f"| merge_state, back to back | bf16 S=32768 H=32 D=128 | {t:.1f} | {by} | "
                f"{by / (t * 1e-6) / 1e9:.0f} | {by / (t * 1e-6) / 8e12 * 100:.1f} |")
@@ -460,7 +461,7 @@ def sweep(torch, mi, inputs, iters, with_cpu=True):
     mso = torch.empty((65536, 8), dtype=torch.float32, device="cuda")
     calls = [Raw(mi, "mi_merge_states", v_, msd, mvo, mso, 65536, 4, 8, 128, mi.MI_F16,
                  mi.MI_F16, st) for v_ in mv]
-    t = _median_us(torch, lambda i: calls[i % 2](), iters)
+    t = _loop_us(torch, lambda i: calls[i % 2](), iters)
     by = 65536 * 8 * (4 * 128 * 2 + 4 * 4 + 128 * 2 + 4)
     out.append(f"| merge_states, back to back | f16 S=65536 N=4 H=8 D=128 | {t:.1f} | {by} | "
                f"{by / (t * 1e-6) / 1e9:.0f} | {by / (t * 1e-6) / 8e12 * 100:.1f} |")
@@ -468,14 +469,14 @@ def sweep(torch, mi, inputs, iters, with_cpu=True):
     torch.cuda.empty_cache()
     sink_calls = [Raw(mi, "mi_merge_sink", va[i], sa[i], sink, va[i], sa[i], 32768, 32, 128,
                       mi.MI_BF16, mi.MI_BF16, st) for i in range(2)]
-    t = _median_us(torch, lambda i: sink_calls[i % 2](), iters)
+    t = _loop_us(torch, lambda i: sink_calls[i % 2](), iters)
     by = rows_ * (2 * 256 + 2 * 4) + 32 * 4
     out.append(f"| merge_sink (in place) | bf16 S=32768 H=32 D=128 | {t:.1f} | {by} | "
                f"{by / (t * 1e-6) / 1e9:.0f} | {by / (t * 1e-6) / 8e12 * 100:.1f} |")
     for label, m, frac in (("all set", ones, 1.0), ("half set", mask, float(mask.float().mean()))):
         calls = [Raw(mi, "mi_merge_state_in_place", va[i], sa[i], vb, sb, m, 32768, 32, 128,
                      mi.MI_BF16, st) for i in range(2)]
-        t = _median_us(torch, lambda i: calls[i % 2](), iters)
+        t = _loop_us(torch, lambda i: calls[i % 2](), iters)
         by = int(rows_ * frac) * (3 * 256 + 3 * 4) + 32768
         out.append(f"| merge_state_in_place, mask {label} | bf16 S=32768 H=32 D=128 | {t:.1f} | "
                    f"{by} | {by / (t * 1e-6) / 1e9:.0f} | {by / (t * 1e-6) / 8e12 * 100:.1f} |")
@@ -483,14 +484,14 @@ def sweep(torch, mi, inputs, iters, with_cpu=True):
     indptr = inputs.segment_indptr(2200, 8192, 8)
     total = int(indptr[-1])
     c = inputs.merge_states_case(2201, S=1, N=total, H=8, D=128, dtype="f16")
-    vv = [to_dev(c["v"].reshape(total, 8, 128), "f16", torch) for _ in range(2)]
+    vv = [to_dev(c["v"].reshape(total, 8, 128), "f16", torch) for _ in range(4)]
     ss = torch.from_numpy(c["s"].reshape(total, 8)).cuda()
     ipd = torch.from_numpy(indptr).cuda()
     vo = torch.empty((8192, 8, 128), dtype=torch.float16, device="cuda")
     so = torch.empty((8192, 8), dtype=torch.float32, device="cuda")
     calls = [Raw(mi, "mi_merge_states_varlen", vv[i], ss, ipd, total, vo, so, 8192, 8, 128,
-                 mi.MI_F16, mi.MI_F16, st) for i in range(2)]
-    t = _median_us(torch, lambda i: calls[i % 2](), iters)
+                 mi.MI_F16, mi.MI_F16, st) for i in range(4)]
+    t = _loop_us(torch, lambda i: calls[i % 4](), iters)
     by = total * 8 * (256 + 4) + 8193 * 4 + 8192 * 8 * (256 + 4)
     out.append(f"| merge_states_varlen | f16 8192 sets x U[0..8] states ({total}), H=8 D=128 | "
                f"{t:.1f} | {by} | {by / (t * 1e-6) / 1e9:.0f} | {by / (t * 1e-6) / 8e12 * 100:.1f} |")
