@@ -47,6 +47,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--ceiling", action="store_true",
+                    help=("run only the plain streaming read (mi_stream_read over 1 GiB and "
+                          "128 MiB) and a 1 GiB device copy: the practical HBM rates the "
+                          "roofline fractions are read against"))
     ap.add_argument("--configs", action="store_true",
                     help=("instead of the step: one JSON line per workload (the two merges, "
                           "decode at B=1 and on the mixed batch, the cascade) with median / "
@@ -501,6 +505,34 @@ def sweep(torch, mi, inputs, iters, with_cpu=True):
     print("\n".join(out))
 
 
+def ceiling(torch, mi, iters):
+    """Practical HBM rates, printed as JSON lines: the library's plain streaming
+    read (mi_stream_read: 16-byte non-temporal loads, nothing else) over 1 GiB
+    and over 128 MiB (the decode's K/V size), and torch's 1 GiB device copy.
+    They are the context for the kernels' fractions of the 8 TB/s peak. Buffers
+    are rotated so that the 256 MB Infinity Cache holds none of the next call's
+    input."""
+    import ctypes
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    xo = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for nbytes, copies in ((1 << 30, 2), (128 << 20, 4)):
+        bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device="cuda") for _ in range(copies)]
+        calls = [Raw(mi, "mi_stream_read", b, nbytes, xo, st) for b in bufs]
+        t = _loop_us(torch, lambda i: calls[i % copies](), iters)
+        print(json.dumps({"kernel": "mi_stream_read (plain 16-byte streaming read)",
+                          "bytes": nbytes, "us": round(t, 2),
+                          "GB/s": round(nbytes / (t * 1e-6) / 1e9, 1),
+                          "frac_of_8TBs": round(nbytes / (t * 1e-6) / 8e12, 4)}))
+        del bufs, calls
+    a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    t = _loop_us(torch, lambda i: b.copy_(a), iters)
+    moved = 2 * a.numel() * 4
+    print(json.dumps({"kernel": "torch device copy: 1 GiB read + 1 GiB written", "bytes": moved,
+                      "us": round(t, 2), "GB/s": round(moved / (t * 1e-6) / 1e9, 1),
+                      "frac_of_8TBs": round(moved / (t * 1e-6) / 8e12, 4)}))
+
+
 def cpu_baseline_sweep(oracle, inputs, ms, sink, indptr, vs_case):
     """The fp64 oracle timed beside the sweep's kernels, on bounded samples of
     the same inputs (cpu_baseline leg of --sweep). GB/s counts the same
@@ -762,6 +794,10 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 5}))
+        return
+
+    if args.ceiling:
+        ceiling(torch, mi, max(args.steps, 20))
         return
 
     if args.configs:

@@ -358,6 +358,20 @@ mi_status mi_cascade_decode(const void* q, const void* k_cache, const void* v_ca
 mi_status mi_prefix_attention_workspace(int32_t R, int32_t Hq, int32_t Hkv, int32_t D,
                                         int32_t prefix_len, size_t* ws_bytes);
 
+/*
+ * Measurement aid, not a step of the method: one plain streaming read of a
+ * buffer. It gives the practical HBM read rate of the device, the context in
+ * which the other kernels' fractions of the peak are read.
+ *   x       : bytes of device memory, 16-byte aligned; bytes a multiple of 16 (>= 0)
+ *   xor_out : one uint32 on the device; *xor_out is XOR-ed with the XOR of all
+ *             32-bit words of x, so a caller that zeroes it first gets that XOR
+ *             (bytes = 0 leaves it unchanged and enqueues nothing)
+ * Errors: MI_ERR_NULL (x or xor_out NULL with bytes > 0), MI_ERR_SHAPE (bytes
+ * negative or not a multiple of 16), MI_ERR_UNSUPPORTED (alignment),
+ * MI_ERR_ALIAS (xor_out inside x).
+ */
+mi_status mi_stream_read(const void* x, int64_t bytes, uint32_t* xor_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

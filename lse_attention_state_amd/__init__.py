@@ -57,6 +57,7 @@ SIGNATURES = {
     "mi_split_kv_decode_varlen": [_P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I64,
                                   _P, _I32, _F, ctypes.c_int, _P, _P, _P, _P, _P, ctypes.c_int,
                                   _P],
+    "mi_stream_read": [_P, _I64, _P, _P],
 }
 
 
@@ -492,3 +493,19 @@ def cascade_decode_fused(q, k_cache, v_cache, prefix_pages, prefix_len: int, suf
           workspace.numel() * 4, _ptr(o_part), _ptr(lse_part), _ptr(counters), _ptr(out),
           _ptr(lse), _dt(out), _stream(q))
     return out, lse
+
+
+# ----------------------------------------------------------------------------- measurement
+
+def stream_read(x, xor_out=None):
+    """One plain streaming read of the contiguous device tensor x (its byte size
+    a multiple of 16): the practical HBM read rate's probe. Returns the uint32
+    XOR of all its 32-bit words as a one-element int32 device tensor, or XOR-s it
+    into the given ``xor_out``."""
+    _check_cuda(x, xor_out)
+    if xor_out is None:
+        xor_out = torch.zeros(1, dtype=torch.int32, device=x.device)
+    if xor_out.dtype != torch.int32 or xor_out.numel() < 1:
+        raise ValueError("stream_read: xor_out must be int32 with one element")
+    _call("mi_stream_read", _ptr(x), x.numel() * x.element_size(), _ptr(xor_out), _stream(x))
+    return xor_out

@@ -643,4 +643,13 @@ mi_status mi_cascade_decode(const void* q, const void* k_cache, const void* v_ca
       counters, o, lse, out_dtype, static_cast<hipStream_t>(stream)));
 }
 
+mi_status mi_stream_read(const void* x, int64_t bytes, uint32_t* xor_out, void* stream) {
+  if (bytes < 0 || bytes % 16 != 0) return MI_ERR_SHAPE;
+  if (bytes == 0) return MI_OK;
+  if (!x || !xor_out) return MI_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(xor_out, 4)) return MI_ERR_UNSUPPORTED;
+  if (overlaps(xor_out, 4, x, bytes)) return MI_ERR_ALIAS;
+  return from_hip(mi::launch_stream_read(x, bytes, xor_out, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -77,4 +77,9 @@ hipError_t launch_prefix_attention(const void* q, const void* kc, const void* vc
                                    float* ws_o, float* ws_s, void* v_out, float* s_out,
                                    int out_dtype, hipStream_t stream);
 
+// Plain streaming read of `bytes` (a multiple of 16) at x; *xor_out ^= the
+// XOR of all its 32-bit words.
+hipError_t launch_stream_read(const void* x, int64_t bytes, uint32_t* xor_out,
+                              hipStream_t stream);
+
 }  // namespace mi

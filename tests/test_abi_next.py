@@ -1,5 +1,6 @@
 """CPU-only checks of the entry points for per-sequence splits, the attention
-sink, the masked in-place merge and the variable-length merge: the host-side
+sink, the masked in-place merge, the variable-length merge and the streaming
+read used for measurement: the host-side
 planner agrees bit-exactly with the oracle's, and argument validation refuses
 bad calls before anything is launched (fake device addresses, never touched).
 """
@@ -167,3 +168,18 @@ def test_merge_states_workspace_and_two_level_validation():
     assert call(ws=P((2 << 30) + 16)) == EALIAS         # workspace over the output
     assert call(N=0) == ESHAPE
     assert call(S=0) == OK
+
+
+def test_stream_read_validation():
+    lib = mi.lib()
+
+    def call(x=P(0), nbytes=1 << 20, out=P(1 << 30)):
+        return lib.mi_stream_read(x, ctypes.c_int64(nbytes), out, NULL)
+    assert call(nbytes=-16) == ESHAPE
+    assert call(nbytes=24) == ESHAPE                     # not a multiple of 16
+    assert call(x=NULL, out=NULL, nbytes=0) == OK        # nothing to read: nothing enqueued
+    assert call(x=NULL) == ENULL
+    assert call(out=NULL) == ENULL
+    assert call(x=P(8)) == EUNSUP                        # 16-byte alignment
+    assert call(out=P((1 << 30) + 2)) == EUNSUP
+    assert call(out=P(4096)) == EALIAS                   # the result word inside the buffer
