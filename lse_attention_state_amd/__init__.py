@@ -101,6 +101,8 @@ def _ptr(t):
 
 
 def _check_cuda(*ts):
+    """Every given tensor is a contiguous GPU tensor on the first one's device."""
+    dev = None
     for t in ts:
         if t is None:
             continue
@@ -108,6 +110,27 @@ def _check_cuda(*ts):
             raise ValueError("tensors must be on the GPU")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("tensors must all be on one GPU")
+
+
+def _expect(t, name, shape=None, dtype=None, numel_at_least=None):
+    """Shape / dtype / size checks of an optional tensor (None passes)."""
+    if t is None:
+        return
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel_at_least is not None and t.numel() < numel_at_least:
+        raise ValueError(f"{name} must have at least {numel_at_least} elements, got {t.numel()}")
+
+
+def _out_dtype_ok(t, name):
+    if t is not None and t.dtype not in _DT:
+        raise TypeError(f"{name}: unsupported dtype {t.dtype}")
 
 
 def _dt(t: torch.Tensor) -> int:
@@ -128,11 +151,19 @@ def merge_state(v_a, s_a, v_b, s_b, out_dtype=None, v_out=None, s_out=None, retu
 
     ``v_out`` may be ``v_a`` or ``v_b`` (in place) when dtypes match; ``s_out``
     may be ``s_a`` or ``s_b``."""
-    _check_cuda(v_a, s_a, v_b, s_b, v_out, s_out)
     _f32(s_a, "s_a"), _f32(s_b, "s_b"), _f32(s_out, "s_out")
+    _dt(v_a)
+    if v_b.dtype != v_a.dtype:
+        raise TypeError("merge_state: v_a and v_b must share one dtype")
     if v_a.shape != v_b.shape or s_a.shape != s_b.shape or v_a.shape[:-1] != s_a.shape:
         raise ValueError("merge_state: shapes must be v [..., D] and s [...] for both states")
+    _out_dtype_ok(v_out, "v_out")
+    _expect(v_out, "v_out", v_a.shape)
+    _expect(s_out, "s_out", s_a.shape)
     out_dtype = out_dtype or (v_out.dtype if v_out is not None else v_a.dtype)
+    if v_out is not None and v_out.dtype != out_dtype:
+        raise TypeError("merge_state: v_out's dtype differs from out_dtype")
+    _check_cuda(v_a, s_a, v_b, s_b, v_out, s_out)
     if v_out is None:
         v_out = torch.empty(v_a.shape, dtype=out_dtype, device=v_a.device)
     if s_out is None and return_s:
@@ -146,12 +177,18 @@ def merge_state(v_a, s_a, v_b, s_b, out_dtype=None, v_out=None, s_out=None, retu
 
 def merge_states(v, s, out_dtype=None, v_out=None, s_out=None, return_s=True):
     """Merge N states: v [S, N, H, D], s [S, N, H] -> (v [S, H, D], s [S, H])."""
-    _check_cuda(v, s, v_out, s_out)
     _f32(s, "s"), _f32(s_out, "s_out")
+    _dt(v)
     if v.dim() != 4 or s.shape != v.shape[:3]:
         raise ValueError("merge_states: v must be [S, N, H, D] and s [S, N, H]")
     S, N, H, D = v.shape
+    _out_dtype_ok(v_out, "v_out")
+    _expect(v_out, "v_out", (S, H, D))
+    _expect(s_out, "s_out", (S, H))
     out_dtype = out_dtype or (v_out.dtype if v_out is not None else v.dtype)
+    if v_out is not None and v_out.dtype != out_dtype:
+        raise TypeError("merge_states: v_out's dtype differs from out_dtype")
+    _check_cuda(v, s, v_out, s_out)
     if v_out is None:
         v_out = torch.empty((S, H, D), dtype=out_dtype, device=v.device)
     if s_out is None and return_s:
@@ -171,17 +208,26 @@ def merge_states_two_level(v, s, out_dtype=None, v_out=None, s_out=None, workspa
                            return_s=True):
     """N-state merge over two levels (few positions, many states):
     v [S, N, H, D], s [S, N, H] -> (v [S, H, D], s [S, H])."""
-    _check_cuda(v, s, v_out, s_out, workspace)
     _f32(s, "s"), _f32(s_out, "s_out"), _f32(workspace, "workspace")
+    _dt(v)
     if v.dim() != 4 or s.shape != v.shape[:3]:
         raise ValueError("merge_states_two_level: v must be [S, N, H, D] and s [S, N, H]")
     S, N, H, D = v.shape
+    _out_dtype_ok(v_out, "v_out")
+    _expect(v_out, "v_out", (S, H, D))
+    _expect(s_out, "s_out", (S, H))
+    need = merge_states_workspace_bytes(S, N, H, D)
+    if workspace is not None and workspace.numel() * 4 < need:
+        raise ValueError(f"merge_states_two_level: workspace holds {workspace.numel() * 4} bytes, "
+                         f"{need} needed")
     out_dtype = out_dtype or (v_out.dtype if v_out is not None else v.dtype)
+    if v_out is not None and v_out.dtype != out_dtype:
+        raise TypeError("merge_states_two_level: v_out's dtype differs from out_dtype")
+    _check_cuda(v, s, v_out, s_out, workspace)
     if v_out is None:
         v_out = torch.empty((S, H, D), dtype=out_dtype, device=v.device)
     if s_out is None and return_s:
         s_out = torch.empty((S, H), dtype=torch.float32, device=v.device)
-    need = merge_states_workspace_bytes(S, N, H, D)
     if workspace is None and need > 0:
         workspace = torch.empty(need // 4, dtype=torch.float32, device=v.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * 4
@@ -193,8 +239,8 @@ def merge_states_two_level(v, s, out_dtype=None, v_out=None, s_out=None, workspa
 def merge_state_in_place(v, s, v_other, s_other, mask=None):
     """v, s <- merge((v, s), (v_other, s_other)) where mask [S] (bool / uint8) is set;
     positions with a zero mask byte are left untouched. v [S, H, D] or [S, D]."""
-    _check_cuda(v, s, v_other, s_other, mask)
     _f32(s, "s"), _f32(s_other, "s_other")
+    _dt(v)
     if v.shape != v_other.shape or s.shape != s_other.shape or v.shape[:-1] != s.shape:
         raise ValueError("merge_state_in_place: v [S, (H,) D] and s [S, (H)] for both states")
     if v.dtype != v_other.dtype:
@@ -207,6 +253,7 @@ def merge_state_in_place(v, s, v_other, s_other, mask=None):
             mask = mask.view(torch.uint8)
         if mask.dtype != torch.uint8 or mask.shape != (S,):
             raise ValueError("mask must be bool or uint8 of shape [S]")
+    _check_cuda(v, s, v_other, s_other, mask)
     _call("mi_merge_state_in_place", _ptr(v), _ptr(s), _ptr(v_other), _ptr(s_other), _ptr(mask),
           S, max(H, 1), D, _dt(v), _stream(v))
     return v, s
@@ -215,12 +262,18 @@ def merge_state_in_place(v, s, v_other, s_other, mask=None):
 def merge_sink(v, s, sink, out_dtype=None, v_out=None, s_out=None, return_s=True):
     """Fold an attention sink (natural-log logit per head, sink [H] float32) into
     states v [S, H, D], s [S, H] -> (v, s). v_out / s_out may be v / s."""
-    _check_cuda(v, s, sink, v_out, s_out)
     _f32(s, "s"), _f32(sink, "sink"), _f32(s_out, "s_out")
+    _dt(v)
     if v.dim() != 3 or s.shape != v.shape[:2] or sink.shape != (v.shape[1],):
         raise ValueError("merge_sink: v [S, H, D], s [S, H], sink [H]")
     S, H, D = v.shape
+    _out_dtype_ok(v_out, "v_out")
+    _expect(v_out, "v_out", v.shape)
+    _expect(s_out, "s_out", s.shape)
     out_dtype = out_dtype or (v_out.dtype if v_out is not None else v.dtype)
+    if v_out is not None and v_out.dtype != out_dtype:
+        raise TypeError("merge_sink: v_out's dtype differs from out_dtype")
+    _check_cuda(v, s, sink, v_out, s_out)
     if v_out is None:
         v_out = torch.empty(v.shape, dtype=out_dtype, device=v.device)
     if s_out is None and return_s:
@@ -233,13 +286,21 @@ def merge_sink(v, s, sink, out_dtype=None, v_out=None, s_out=None, return_s=True
 def merge_states_varlen(v, s, indptr, out_dtype=None, v_out=None, s_out=None, return_s=True):
     """Merge variable-length index sets: v [total, H, D], s [total, H], indptr [S+1]
     int32 (device) -> (v [S, H, D], s [S, H])."""
-    _check_cuda(v, s, indptr, v_out, s_out)
     _f32(s, "s"), _f32(s_out, "s_out")
-    if v.dim() != 3 or s.shape != v.shape[:2] or indptr.dim() != 1 or indptr.dtype != torch.int32:
+    _dt(v)
+    if indptr.dtype != torch.int32:
+        raise TypeError("merge_states_varlen: indptr must be int32")
+    if v.dim() != 3 or s.shape != v.shape[:2] or indptr.dim() != 1 or indptr.shape[0] < 1:
         raise ValueError("merge_states_varlen: v [total, H, D], s [total, H], indptr int32 [S+1]")
     total, H, D = v.shape
     S = indptr.shape[0] - 1
+    _out_dtype_ok(v_out, "v_out")
+    _expect(v_out, "v_out", (S, H, D))
+    _expect(s_out, "s_out", (S, H))
     out_dtype = out_dtype or (v_out.dtype if v_out is not None else v.dtype)
+    if v_out is not None and v_out.dtype != out_dtype:
+        raise TypeError("merge_states_varlen: v_out's dtype differs from out_dtype")
+    _check_cuda(v, s, indptr, v_out, s_out)
     if v_out is None:
         v_out = torch.empty((S, H, D), dtype=out_dtype, device=v.device)
     if s_out is None and return_s:
@@ -282,7 +343,6 @@ def split_range(ctx: int, page_size: int, num_splits: int, split: int):
 # ----------------------------------------------------------------------------- decode
 
 def _decode_args(q, k_cache, v_cache, page_table, ctx_lens):
-    _check_cuda(q, k_cache, v_cache, page_table, ctx_lens)
     if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
         raise ValueError("q must be [B, Hq, D] and k/v caches [pages, Hkv, PAGE, D]")
     if q.dtype != k_cache.dtype or k_cache.dtype != v_cache.dtype:
@@ -296,15 +356,27 @@ def _decode_args(q, k_cache, v_cache, page_table, ctx_lens):
     return B, Hq, Hkv, D, page, P
 
 
+def _decode_outputs(B, Hq, Hkv, D, parts, o_part, lse_part, out=None, lse=None, counters=None):
+    """Checks of caller-given decode outputs and workspaces: parts is the shape
+    prefix of the partials ((B, Hq, splits) or (total, Hq))."""
+    _expect(o_part, "o_part", (*parts, D), torch.float32)
+    _expect(lse_part, "lse_part", parts, torch.float32)
+    _out_dtype_ok(out, "out")
+    _expect(out, "out", (B, Hq, D))
+    _expect(lse, "lse", (B, Hq), torch.float32)
+    _expect(counters, "counters", None, torch.int32, B * Hkv)
+
+
 def split_kv_partial(q, k_cache, v_cache, page_table, ctx_lens, num_splits: int, sm_scale: float,
                      o_part=None, lse_part=None):
     """Pass 1 only -> (o_part [B, Hq, splits, D] f32, lse_part [B, Hq, splits] f32)."""
     B, Hq, Hkv, D, page, P = _decode_args(q, k_cache, v_cache, page_table, ctx_lens)
+    _decode_outputs(B, Hq, Hkv, D, (B, Hq, num_splits), o_part, lse_part)
+    _check_cuda(q, k_cache, v_cache, page_table, ctx_lens, o_part, lse_part)
     if o_part is None:
         o_part = torch.empty((B, Hq, num_splits, D), dtype=torch.float32, device=q.device)
     if lse_part is None:
         lse_part = torch.empty((B, Hq, num_splits), dtype=torch.float32, device=q.device)
-    _check_cuda(o_part, lse_part)
     _call("mi_split_kv_partial", _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
           page_table.shape[1], _ptr(ctx_lens), B, Hq, Hkv, D, page, P, num_splits,
           float(sm_scale), _dt(q), _ptr(o_part), _ptr(lse_part), _stream(q))
@@ -316,6 +388,8 @@ def split_kv_decode(q, k_cache, v_cache, page_table, ctx_lens, num_splits: int, 
                     return_lse=True, return_partials=False):
     """Both passes -> (o [B, Hq, D], lse [B, Hq] f32 base 2[, o_part, lse_part])."""
     B, Hq, Hkv, D, page, P = _decode_args(q, k_cache, v_cache, page_table, ctx_lens)
+    _decode_outputs(B, Hq, Hkv, D, (B, Hq, num_splits), o_part, lse_part, out, lse)
+    _check_cuda(q, k_cache, v_cache, page_table, ctx_lens, o_part, lse_part, out, lse)
     out_dtype = out_dtype or (out.dtype if out is not None else q.dtype)
     if o_part is None:
         o_part = torch.empty((B, Hq, num_splits, D), dtype=torch.float32, device=q.device)
@@ -325,7 +399,6 @@ def split_kv_decode(q, k_cache, v_cache, page_table, ctx_lens, num_splits: int, 
         out = torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
     if lse is None and return_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    _check_cuda(o_part, lse_part, out, lse)
     _call("mi_split_kv_decode", _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
           page_table.shape[1], _ptr(ctx_lens), B, Hq, Hkv, D, page, P, num_splits,
           float(sm_scale), _dt(q), _ptr(o_part), _ptr(lse_part), _ptr(out), _ptr(lse),
@@ -345,11 +418,11 @@ def split_kv_decode_fused(q, k_cache, v_cache, page_table, ctx_lens, num_splits:
     the first call; each call leaves it zero. It is allocated (zeroed) when not
     given."""
     B, Hq, Hkv, D, page, P = _decode_args(q, k_cache, v_cache, page_table, ctx_lens)
+    _decode_outputs(B, Hq, Hkv, D, (B, Hq, num_splits), o_part, lse_part, out, lse, counters)
+    _check_cuda(q, k_cache, v_cache, page_table, ctx_lens, o_part, lse_part, out, lse, counters)
     out_dtype = out_dtype or (out.dtype if out is not None else q.dtype)
     if counters is None:
         counters = torch.zeros((B, Hkv), dtype=torch.int32, device=q.device)
-    if counters.dtype != torch.int32 or counters.numel() < B * Hkv:
-        raise ValueError("counters must be int32 with at least B * Hkv entries")
     if o_part is None:
         o_part = torch.empty((B, Hq, num_splits, D), dtype=torch.float32, device=q.device)
     if lse_part is None:
@@ -358,7 +431,6 @@ def split_kv_decode_fused(q, k_cache, v_cache, page_table, ctx_lens, num_splits:
         out = torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
     if lse is None and return_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    _check_cuda(o_part, lse_part, out, lse, counters)
     _call("mi_split_kv_decode_fused", _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
           page_table.shape[1], _ptr(ctx_lens), B, Hq, Hkv, D, page, P, num_splits,
           float(sm_scale), _dt(q), _ptr(o_part), _ptr(lse_part), _ptr(counters), _ptr(out),
@@ -379,20 +451,29 @@ def split_kv_decode_varlen(q, k_cache, v_cache, page_table, ctx_lens, split_indp
     import numpy as np
     B, Hq, Hkv, D, page, P = _decode_args(q, k_cache, v_cache, page_table, ctx_lens)
     if isinstance(split_indptr, np.ndarray):
+        if split_indptr.shape != (B + 1,):
+            raise ValueError("split_indptr must be int32 [B + 1]")
         total = int(split_indptr[-1])
-        split_indptr = torch.from_numpy(np.ascontiguousarray(split_indptr, np.int32)).to(q.device)
     else:
+        if split_indptr.dtype != torch.int32 or split_indptr.shape != (B + 1,):
+            raise ValueError("split_indptr must be int32 [B + 1]")
+        total = None
+    if not fused:
+        counters = None
+    if total is not None:
+        _decode_outputs(B, Hq, Hkv, D, (total, Hq), o_part, lse_part, out, lse, counters)
+    else:
+        _decode_outputs(B, Hq, Hkv, D, (B, Hq), None, None, out, lse, counters)
+    _check_cuda(q, k_cache, v_cache, page_table, ctx_lens, o_part, lse_part, out, lse, counters,
+                None if total is not None else split_indptr)
+    if total is None:
         total = int(split_indptr[-1].item())
-    _check_cuda(split_indptr)
-    if split_indptr.dtype != torch.int32 or split_indptr.shape != (B + 1,):
-        raise ValueError("split_indptr must be int32 [B + 1]")
+        _decode_outputs(B, Hq, Hkv, D, (total, Hq), o_part, lse_part)
+    else:
+        split_indptr = torch.from_numpy(np.ascontiguousarray(split_indptr, np.int32)).to(q.device)
     out_dtype = out_dtype or (out.dtype if out is not None else q.dtype)
     if fused and counters is None:
         counters = torch.zeros((B, Hkv), dtype=torch.int32, device=q.device)
-    if not fused:
-        counters = None
-    if counters is not None and (counters.dtype != torch.int32 or counters.numel() < B * Hkv):
-        raise ValueError("counters must be int32 with at least B * Hkv entries")
     if o_part is None:
         o_part = torch.empty((total, Hq, D), dtype=torch.float32, device=q.device)
     if lse_part is None:
@@ -401,7 +482,6 @@ def split_kv_decode_varlen(q, k_cache, v_cache, page_table, ctx_lens, split_indp
         out = torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
     if lse is None and return_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    _check_cuda(o_part, lse_part, out, lse, counters)
     _call("mi_split_kv_decode_varlen", _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
           page_table.shape[1], _ptr(ctx_lens), B, Hq, Hkv, D, page, P, _ptr(split_indptr), total,
           float(sm_scale), _dt(q), _ptr(o_part), _ptr(lse_part), _ptr(counters), _ptr(out),
@@ -423,21 +503,31 @@ def prefix_attention(q, k_cache, v_cache, prefix_pages, prefix_len: int, sm_scal
                      out_dtype=torch.float32, workspace=None, v_out=None, s_out=None):
     """Cascade level 0: every (request, head) of q [R, Hq, D] against the shared
     prefix pages -> (v [R, Hq, D] out_dtype, s [R, Hq] f32 base 2)."""
-    _check_cuda(q, k_cache, v_cache, prefix_pages, v_out, s_out)
     if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
         raise ValueError("q must be [R, Hq, D] and k/v caches [pages, Hkv, PAGE, D]")
+    if q.dtype != k_cache.dtype or k_cache.dtype != v_cache.dtype:
+        raise TypeError("q, k_cache and v_cache must share one dtype")
     if prefix_pages.dtype != torch.int32:
         raise TypeError("prefix_pages must be int32")
     R, Hq, D = q.shape
     P, Hkv, page, _ = k_cache.shape
+    if prefix_len < 0 or k_cache.shape[3] != D:
+        raise ValueError("prefix_attention: prefix_len must be >= 0 and q's D the caches' D")
+    _expect(prefix_pages, "prefix_pages", None, None, -(-prefix_len // page))
     need = prefix_attention_workspace_bytes(R, Hq, Hkv, D, prefix_len)
+    _expect(workspace, "workspace", None, torch.float32, (need + 3) // 4)
+    _out_dtype_ok(v_out, "v_out")
+    _expect(v_out, "v_out", (R, Hq, D))
+    _expect(s_out, "s_out", (R, Hq), torch.float32)
+    _check_cuda(q, k_cache, v_cache, prefix_pages, v_out, s_out, workspace)
+    if v_out is not None:
+        out_dtype = v_out.dtype
     if workspace is None:
         workspace = torch.empty(max(need // 4, 1), dtype=torch.float32, device=q.device)
     if v_out is None:
         v_out = torch.empty((R, Hq, D), dtype=out_dtype, device=q.device)
     if s_out is None:
         s_out = torch.empty((R, Hq), dtype=torch.float32, device=q.device)
-    _check_cuda(workspace)
     _call("mi_prefix_attention", _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(prefix_pages),
           prefix_len, R, Hq, Hkv, D, page, P, float(sm_scale), _dt(q), _ptr(workspace),
           workspace.numel() * 4, _ptr(v_out), _ptr(s_out), _dt(v_out), _stream(q))
@@ -464,16 +554,27 @@ def cascade_decode_fused(q, k_cache, v_cache, prefix_pages, prefix_len: int, suf
     """Two-level cascade decode in two launches (prefix level on the matrix cores,
     then the suffix decode whose combine also merges the prefix chunk states)
     -> (o [R, Hq, D], lse [R, Hq])."""
-    _check_cuda(q, k_cache, v_cache, prefix_pages, suffix_table, suffix_lens)
     if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
         raise ValueError("q must be [R, Hq, D] and k/v caches [pages, Hkv, PAGE, D]")
+    if q.dtype != k_cache.dtype or k_cache.dtype != v_cache.dtype:
+        raise TypeError("q, k_cache and v_cache must share one dtype")
     if prefix_pages.dtype != torch.int32 or suffix_table.dtype != torch.int32 or \
             suffix_lens.dtype != torch.int32:
         raise TypeError("page lists, tables and lengths must be int32")
     R, Hq, D = q.shape
     P, Hkv, page, _ = k_cache.shape
-    out_dtype = out_dtype or (out.dtype if out is not None else q.dtype)
+    if prefix_len < 0 or k_cache.shape[3] != D:
+        raise ValueError("cascade_decode_fused: prefix_len must be >= 0 and q's D the caches' D")
+    if suffix_table.dim() != 2 or suffix_table.shape[0] != R or suffix_lens.shape != (R,):
+        raise ValueError("cascade_decode_fused: suffix_table must be [R, stride] and "
+                         "suffix_lens [R]")
+    _expect(prefix_pages, "prefix_pages", None, None, -(-prefix_len // page))
     need = prefix_attention_workspace_bytes(R, Hq, Hkv, D, prefix_len)
+    _expect(workspace, "workspace", None, torch.float32, (need + 3) // 4)
+    _decode_outputs(R, Hq, Hkv, D, (R, Hq, suffix_splits), o_part, lse_part, out, lse, counters)
+    _check_cuda(q, k_cache, v_cache, prefix_pages, suffix_table, suffix_lens, workspace, o_part,
+                lse_part, counters, out, lse)
+    out_dtype = out_dtype or (out.dtype if out is not None else q.dtype)
     if workspace is None:
         workspace = torch.empty(max(need // 4, 1), dtype=torch.float32, device=q.device)
     if o_part is None:
@@ -486,7 +587,6 @@ def cascade_decode_fused(q, k_cache, v_cache, prefix_pages, prefix_len: int, suf
         out = torch.empty((R, Hq, D), dtype=out_dtype, device=q.device)
     if lse is None and return_lse:
         lse = torch.empty((R, Hq), dtype=torch.float32, device=q.device)
-    _check_cuda(workspace, o_part, lse_part, counters, out, lse)
     _call("mi_cascade_decode", _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(prefix_pages),
           prefix_len, _ptr(suffix_table), suffix_table.shape[1], _ptr(suffix_lens), R, Hq, Hkv,
           D, page, P, suffix_splits, float(sm_scale), _dt(q), _ptr(workspace),
@@ -502,10 +602,9 @@ def stream_read(x, xor_out=None):
     a multiple of 16): the practical HBM read rate's probe. Returns the uint32
     XOR of all its 32-bit words as a one-element int32 device tensor, or XOR-s it
     into the given ``xor_out``."""
+    _expect(xor_out, "xor_out", None, torch.int32, 1)
     _check_cuda(x, xor_out)
     if xor_out is None:
         xor_out = torch.zeros(1, dtype=torch.int32, device=x.device)
-    if xor_out.dtype != torch.int32 or xor_out.numel() < 1:
-        raise ValueError("stream_read: xor_out must be int32 with one element")
     _call("mi_stream_read", _ptr(x), x.numel() * x.element_size(), _ptr(xor_out), _stream(x))
     return xor_out
