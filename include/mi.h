@@ -281,9 +281,12 @@ mi_status mi_plan_splits_varlen(int32_t B, int32_t Hkv, const int32_t* ctx_lens_
  *   o            : [B, Hq, D] of out_dtype;  lse : [B, Hq] fp32 base 2 (may be NULL)
  * Other arguments, layouts, clamping of device data and supported sizes as in
  * mi_split_kv_partial; additionally B <= 4031 and total_splits <= 65535.
- * A sequence given no split (equal consecutive split_indptr entries) is
- * written (0, -inf) by the two-launch path and left unwritten by the
- * single-launch path.
+ * A sequence given no split (equal consecutive split_indptr entries) gets the
+ * empty state o = 0, lse = -inf in both forms. split_indptr must be
+ * non-decreasing; rows past split_indptr[B] (when total_splits is larger)
+ * belong to no sequence: their partials are written as empty states and they
+ * take no part in any combine. Inconsistent device data never leads to a
+ * read or write outside the arguments' extents.
  */
 mi_status mi_split_kv_decode_varlen(const void* q, const void* k_cache, const void* v_cache,
                                     const int32_t* page_table, int32_t pt_stride,

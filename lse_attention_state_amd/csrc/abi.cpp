@@ -501,7 +501,7 @@ mi_status mi_split_kv_decode_varlen(const void* q, const void* k_cache, const vo
                                     float* lse_part, int32_t* counters, void* o, float* lse,
                                     mi_dtype out_dtype, void* stream) {
   if (!o || !split_indptr) return MI_ERR_NULL;
-  if (B < 0 || total_splits < 0 || (B > 0 && total_splits < B)) return MI_ERR_SHAPE;
+  if (B < 0 || total_splits < 0) return MI_ERR_SHAPE;
   if (B > kMaxVarlenSeqs || total_splits > kMaxVarlenSplits) return MI_ERR_UNSUPPORTED;
   DecodeShape shp;
   mi_status st = check_decode(q, k_cache, v_cache, page_table, pt_stride, ctx_lens, B, Hq, Hkv, D,
@@ -521,6 +521,9 @@ mi_status mi_split_kv_decode_varlen(const void* q, const void* k_cache, const vo
     return MI_ERR_ALIAS;
   if (B == 0) return MI_OK;
   const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (total_splits == 0)  // no work item: every sequence is empty, the combine writes (0, -inf)
+    return from_hip(mi::launch_merge_segments(o_part, lse_part, split_indptr, 0, 0, o, lse, B, Hq,
+                                              D, MI_F32, out_dtype, hs));
   hipError_t e = mi::launch_split_kv_partial_varlen(
       q, k_cache, v_cache, page_table, pt_stride, ctx_lens, B, Hq, Hkv, num_phys_pages,
       split_indptr, total_splits, sm_scale, kv_dtype, o_part, lse_part, hs, counters, o, lse,

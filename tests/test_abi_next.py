@@ -131,7 +131,7 @@ def test_split_kv_decode_varlen_validation():
     assert _vdec(ip=NULL) == ENULL
     assert _vdec(o=NULL) == ENULL
     assert _vdec(op=NULL) == ENULL
-    assert _vdec(total=3) == ESHAPE                # fewer splits than sequences
+    assert _vdec(total=-1) == ESHAPE
     assert _vdec(B=-1) == ESHAPE
     assert _vdec(B=5000, total=5000) == EUNSUP     # beyond the segment search
     assert _vdec(total=70000) == EUNSUP            # beyond the grid height

@@ -333,6 +333,78 @@ def test_varlen_decode_many_sequences(fused, B):
     _check_varlen(case, indptr, fused)
 
 
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_varlen_decode_sequences_without_splits(fused, dtype):
+    """Sequences given no split (equal consecutive split_indptr entries) at the
+    start, in the middle and at the end of the batch come out as the empty
+    state (0, -inf) in both launch forms, with every output pre-filled with
+    NaN; the other sequences' partials and outputs match the oracle."""
+    _say("varlen decode, sequences without splits", fused, dtype)
+    ctx = np.array([40, 300, 17, 1000, 5, 64, 33], np.int32)
+    case = inputs.paged_kv_case(610, ctx, 16, 4, 128, 16, dtype=dtype)
+    counts = np.array([0, 2, 0, 3, 1, 0, 0], np.int32)
+    indptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    out, lse, o_part, lse_part = _varlen_decode(case, indptr, fused)
+    args = (case["q"], case["k"], case["v"], case["page_table"], case["ctx_lens"], case["sm_scale"])
+    o, s = oracle.attention(*args, dtype, dtype)
+    empty = counts == 0
+    o[empty] = 0.0
+    s[empty] = -np.inf
+    check_values(out, o, "o")
+    check_lse(lse, s, "lse")
+    keep = np.flatnonzero(~empty)
+    sub = (np.ascontiguousarray(case["q"][keep]), case["k"], case["v"],
+           np.ascontiguousarray(case["page_table"][keep]), np.ascontiguousarray(ctx[keep]),
+           case["sm_scale"])
+    sub_indptr = np.concatenate([[0], np.cumsum(counts[keep])]).astype(np.int32)
+    op, sp = oracle.split_partials_varlen(*sub, sub_indptr, dtype, dtype)
+    check_values(o_part, op, "o_part")
+    check_lse(lse_part, sp, "lse_part")
+
+
+def test_varlen_decode_items_past_the_index_array():
+    """total_splits larger than split_indptr[B] (inconsistent device data): the
+    extra work items write empty partial rows and leave the counters alone, so
+    the counters come back zero, the outputs match the consistent call, and a
+    second call gives the same result."""
+    import ctypes
+    _say("varlen decode, items past the index array")
+    ctx = np.array([100, 33, 700], np.int32)
+    case = inputs.paged_kv_case(620, ctx, 32, 8, 128, 16, dtype="f16")
+    q, k, v, pt, ctxd = _dev(case)
+    B, Hq, D = q.shape
+    counts = np.array([2, 1, 4], np.int32)
+    indptr_h = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    indptr = torch.from_numpy(indptr_h).cuda()
+    total = int(indptr_h[-1]) + 3
+    nan = float("nan")
+    counters = torch.zeros((B, 8), dtype=torch.int32, device="cuda")
+    res = []
+    for _ in range(2):
+        o_part = torch.full((total, Hq, D), nan, dtype=torch.float32, device="cuda")
+        lse_part = torch.full((total, Hq), nan, dtype=torch.float32, device="cuda")
+        out = torch.full((B, Hq, D), nan, dtype=torch.float16, device="cuda")
+        lse = torch.full((B, Hq), nan, dtype=torch.float32, device="cuda")
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        p = lambda t: ctypes.c_void_p(t.data_ptr())
+        rc = mi.lib().mi_split_kv_decode_varlen(
+            p(q), p(k), p(v), p(pt), pt.shape[1], p(ctxd), B, Hq, 8, D, 16, k.shape[0], p(indptr),
+            total, ctypes.c_float(case["sm_scale"]), mi.MI_F16, p(o_part), p(lse_part),
+            p(counters), p(out), p(lse), mi.MI_F16, st)
+        assert rc == 0
+        torch.cuda.synchronize()
+        assert not counters.any(), "counters must be left zero"
+        extra_o, extra_s = host64(o_part[total - 3:]), host64(lse_part[total - 3:])
+        assert np.all(extra_o == 0) and np.all(np.isneginf(extra_s))
+        res.append((out.clone(), lse.clone()))
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+    args = (case["q"], case["k"], case["v"], case["page_table"], case["ctx_lens"], case["sm_scale"])
+    o, s = oracle.attention(*args, "f16", "f16")
+    check_values(res[0][0], o, "o")
+    check_lse(res[0][1], s, "lse")
+
+
 @pytest.mark.parametrize("S,N,H,dt", [(64, 1024, 1, "f32"), (4, 3000, 2, "f16"), (1, 5000, 1, "bf16"),
                                       (32, 64, 1, "f32"), (8, 200, 3, "f32")])
 def test_merge_states_two_level(S, N, H, dt):
