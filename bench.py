@@ -363,8 +363,12 @@ def sweep(torch, mi, inputs, iters, with_cpu=True):
                  ("8 x 4096", np.full(8, 4096, np.int32)),
                  ("64 x 1024", np.full(64, 1024, np.int32)),
                  ("mixed 32 x U[1,8192]", inputs.mixed_ctx_lens(1004, 32))]
-    out += ["| workload | plan | splits (total) | two launches µs | one launch µs | one launch GB/s |",
-            "|---|---|---:|---:|---:|---:|"]
+    out += ["The fused entry points (mi_split_kv_decode_fused, mi_split_kv_decode_varlen with "
+            "counters) run one launch while the work items (B * Hkv * splits) are at most twice "
+            "the compute units, else pass 1 and the combine as two launches; the form column "
+            "says which.", "",
+            "| workload | plan | splits (total) | two launches µs | fused entry µs | form | "
+            "fused GB/s |", "|---|---|---:|---:|---:|---|---:|"]
     for wi, (name, ctx) in enumerate(workloads):
         case = inputs.paged_kv_case(2000 + wi, ctx, Hq, Hkv, D, PAGE, dtype="f16")
         B = len(ctx)
@@ -393,7 +397,8 @@ def sweep(torch, mi, inputs, iters, with_cpu=True):
             t1 = _loop_us(torch, lambda i: one[i % 4](), iters)
             part = B * Hq * n * (D + 1) * 4 * 2 if n > 1 else 0
             label = "uniform" + (" (planner's pick)" if n == pick else "")
-            rows.append(f"| {name} | {label} | {n} | {t2:.1f} | {t1:.1f} | "
+            form = "one" if n == 1 or B * Hkv * n <= 2 * cus else "two"
+            rows.append(f"| {name} | {label} | {n} | {t2:.1f} | {t1:.1f} | {form} | "
                         f"{(kv_bytes + part) / (t1 * 1e-6) / 1e9:.0f} |")
         indptr = mi.plan_splits_varlen(ctx, Hkv, PAGE)
         total = int(indptr[-1])
@@ -410,8 +415,10 @@ def sweep(torch, mi, inputs, iters, with_cpu=True):
         t1 = _loop_us(torch, lambda i: vone[i % 4](), iters)
         counts = np.diff(indptr)
         part = Hq * total * (D + 1) * 4 * 2 if total > B else 0
+        form = "one" if total * Hkv <= 2 * cus else "two"
         rows.append(f"| {name} | per-sequence (counts {counts.min()}..{counts.max()}) | "
-                    f"({total}) | {t2:.1f} | {t1:.1f} | {(kv_bytes + part) / (t1 * 1e-6) / 1e9:.0f} |")
+                    f"({total}) | {t2:.1f} | {t1:.1f} | {form} | "
+                    f"{(kv_bytes + part) / (t1 * 1e-6) / 1e9:.0f} |")
         out += rows
         del kv, k0, v0
         torch.cuda.empty_cache()

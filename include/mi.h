@@ -233,6 +233,11 @@ mi_status mi_split_kv_decode(const void* q, const void* k_cache, const void* v_c
  * the last workgroup to finish for each (sequence, kv head) merges the splits
  * of that kv head's query heads and writes o and lse. Same results as
  * mi_split_kv_decode up to the order of rounding; saves the second launch.
+ * Launch form: the single launch is used while the work items B * Hkv *
+ * num_splits are at most twice the device's compute units; with more, the
+ * per-workgroup hand-off costs more than a second launch (the same page,
+ * section 6: more splits add intermediates), so pass 1 and the combine run as
+ * the two launches of mi_split_kv_decode and the counters are not touched.
  *   counters : [B, Hkv] int32 device workspace used to find the last
  *              workgroup. It must be all zero before the first call; every call
  *              leaves it all zero again. Calls that share one counters buffer
@@ -275,8 +280,10 @@ mi_status mi_plan_splits_varlen(int32_t B, int32_t Hkv, const int32_t* ctx_lens_
  *   counters     : [B, Hkv] int32 device workspace, or NULL. NULL: two
  *                  launches (pass 1, then mi_merge_states_varlen as the
  *                  combine). Given: one launch whose last workgroup per
- *                  (sequence, kv head) merges the splits; the counters must be
- *                  all zero before the first call and every call leaves them
+ *                  (sequence, kv head) merges the splits, while the work items
+ *                  total_splits * Hkv are at most twice the device's compute
+ *                  units (two launches beyond, as for NULL); the counters must
+ *                  be all zero before the first call and every call leaves them
  *                  zero; calls sharing them must not run concurrently.
  *   o            : [B, Hq, D] of out_dtype;  lse : [B, Hq] fp32 base 2 (may be NULL)
  * Other arguments, layouts, clamping of device data and supported sizes as in

@@ -39,6 +39,32 @@ bool bad_alias(const void* out, int64_t out_bytes, const void* in, int64_t in_by
 
 mi_status from_hip(hipError_t e) { return e == hipSuccess ? MI_OK : MI_ERR_HIP; }
 
+// Compute units of the current device, cached per device (the only state the
+// library keeps; concurrent first calls store the same value).
+mi_status device_cus(int* cus) {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MI_ERR_HIP;
+  if (dev >= 0 && dev < 64 && cached[dev] > 0) {
+    *cus = cached[dev];
+    return MI_OK;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return MI_ERR_HIP;
+  if (dev >= 0 && dev < 64) cached[dev] = n;
+  *cus = n;
+  return MI_OK;
+}
+
+// The single-launch decode pays, in every workgroup, a wait for its partials
+// to complete and a device-scope counter update, and in the last workgroup of
+// each (sequence, kv head) an L2 invalidation that the other workgroups' K/V
+// streams feel. Measured on MI355X (the L3 page's three workloads and the
+// mixed batch at 1-64 splits), it beats pass 1 plus a separate combine launch
+// while the work items are at most twice the compute units, and loses beyond.
+bool single_launch_pays(int64_t work_items, int cus) { return work_items <= 2 * int64_t(cus); }
+
 // Products of validated non-negative sizes stay below 2^62 bytes.
 bool size_ok(int64_t a, int64_t b, int64_t c = 1, int64_t d = 1) {
   const int64_t lim = int64_t(1) << 62;
@@ -196,13 +222,7 @@ mi_status mi_plan_splits(int32_t B, int32_t Hkv, const int32_t* ctx_lens_host, i
     const int np = mi::ceil_div(ctx_lens_host[b], page_size);
     if (np > max_pages) max_pages = np;
   }
-  if (num_cus <= 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        num_cus <= 0)
-      return MI_ERR_HIP;
-  }
+  if (num_cus <= 0 && device_cus(&num_cus) != MI_OK) return MI_ERR_HIP;
   // "L3 hints", section 6: enough workgroups to fill the device a few times
   // over (here: twice the compute units), but no split thinner than 8 pages.
   static const int kChoices[4] = {1, 4, 16, 64};
@@ -315,11 +335,21 @@ mi_status mi_split_kv_decode_fused(const void* q, const void* k_cache, const voi
                             true, o, lse, B, Hq, Hkv, D, out_dtype, shp);
   if (st != MI_OK) return st;
   if (B == 0) return MI_OK;
+  int cus = 0;
+  if (device_cus(&cus) != MI_OK) return MI_ERR_HIP;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (num_splits > 1 && !single_launch_pays(int64_t(B) * Hkv * num_splits, cus)) {
+    hipError_t e = mi::launch_split_kv_partial(q, k_cache, v_cache, page_table, pt_stride,
+                                               ctx_lens, B, Hq, Hkv, num_phys_pages, num_splits,
+                                               sm_scale, kv_dtype, o_part, lse_part, hs);
+    if (e != hipSuccess) return MI_ERR_HIP;
+    return from_hip(mi::launch_merge_states(o_part, lse_part, o, lse, int64_t(B) * Hq, num_splits,
+                                            1, D, MI_F32, out_dtype, hs));
+  }
   return from_hip(mi::launch_split_kv_partial(q, k_cache, v_cache, page_table, pt_stride,
                                               ctx_lens, B, Hq, Hkv, num_phys_pages, num_splits,
-                                              sm_scale, kv_dtype, o_part, lse_part,
-                                              static_cast<hipStream_t>(stream), counters, o, lse,
-                                              out_dtype));
+                                              sm_scale, kv_dtype, o_part, lse_part, hs, counters,
+                                              o, lse, out_dtype));
 }
 
 mi_status mi_merge_states_workspace(int64_t S, int32_t N, int32_t H, int32_t D,
@@ -449,13 +479,7 @@ mi_status mi_plan_splits_varlen(int32_t B, int32_t Hkv, const int32_t* ctx_lens_
     const int64_t np = (int64_t(ctx_lens_host[b]) + page_size - 1) / page_size;
     if (np > max_np) max_np = np;
   }
-  if (num_cus <= 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        num_cus <= 0)
-      return MI_ERR_HIP;
-  }
+  if (num_cus <= 0 && device_cus(&num_cus) != MI_OK) return MI_ERR_HIP;
   // Work items when every split holds at most c pages; never increases with c.
   auto items = [&](int64_t c) {
     int64_t w = 0;
@@ -524,6 +548,11 @@ mi_status mi_split_kv_decode_varlen(const void* q, const void* k_cache, const vo
   if (total_splits == 0)  // no work item: every sequence is empty, the combine writes (0, -inf)
     return from_hip(mi::launch_merge_segments(o_part, lse_part, split_indptr, 0, 0, o, lse, B, Hq,
                                               D, MI_F32, out_dtype, hs));
+  if (counters != nullptr) {
+    int cus = 0;
+    if (device_cus(&cus) != MI_OK) return MI_ERR_HIP;
+    if (!single_launch_pays(int64_t(total_splits) * Hkv, cus)) counters = nullptr;
+  }
   hipError_t e = mi::launch_split_kv_partial_varlen(
       q, k_cache, v_cache, page_table, pt_stride, ctx_lens, B, Hq, Hkv, num_phys_pages,
       split_indptr, total_splits, sm_scale, kv_dtype, o_part, lse_part, hs, counters, o, lse,

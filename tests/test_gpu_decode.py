@@ -255,3 +255,53 @@ def test_decode_maximum_split_count(fused):
     check_lse(lse_part, sp, "lse_part")
     check_values(out, o, "o")
     check_lse(lse, s, "lse")
+
+
+@pytest.mark.parametrize("splits", [100, 500])
+def test_fused_decode_many_splits_single_launch(splits):
+    """Few work items but many splits (B=1, Hkv=1, Hq=4): the single launch is
+    used and its last workgroup merges more than 64 splits per row, in several
+    passes."""
+    _say("fused decode many splits, one launch", splits)
+    ctx = np.array([16000], np.int32)
+    case = inputs.paged_kv_case(70 + splits, ctx, 4, 1, 128, 16, dtype="f16")
+    out, lse, o_part, lse_part = _decode_fused(case, splits)
+    o, s, op, sp = _oracle(case, splits)
+    check_values(o_part, op, "o_part")
+    check_lse(lse_part, sp, "lse_part")
+    check_values(out, o, "o")
+    check_lse(lse, s, "lse")
+
+
+_SWEEP_CACHE = {}
+
+
+def _sweep_case(name):
+    """The L3 page's 8 x 4096 and 64 x 1024 workloads (Hq=32, Hkv=8, fp16,
+    random page permutation), as the split sweep times them."""
+    if name not in _SWEEP_CACHE:
+        B, ctx_len = {"8x4096": (8, 4096), "64x1024": (64, 1024)}[name]
+        ctx = np.full(B, ctx_len, np.int32)
+        case = inputs.paged_kv_case(2000 + B, ctx, 32, 8, 128, 16, dtype="f16")
+        args = (case["q"], case["k"], case["v"], case["page_table"], case["ctx_lens"],
+                case["sm_scale"])
+        _SWEEP_CACHE[name] = (case, oracle.attention(*args, "f16", "f16"))
+    return _SWEEP_CACHE[name]
+
+
+@pytest.mark.parametrize("name", ["8x4096", "64x1024"])
+@pytest.mark.parametrize("splits", [1, 4, 16, 64])
+def test_decode_sweep_workloads(name, splits):
+    """The split sweep's own workloads at every split count it times, in both
+    launch forms: partials in full against the oracle's per-split partials,
+    outputs in full against unsplit attention."""
+    _say("decode sweep workload", name, splits)
+    case, (o, s) = _sweep_case(name)
+    args = (case["q"], case["k"], case["v"], case["page_table"], case["ctx_lens"], case["sm_scale"])
+    op, sp = oracle.split_partials(*args, splits, "f16", "f16")
+    for fused in (False, True):
+        out, lse, o_part, lse_part = (_decode_fused if fused else _decode)(case, splits)
+        check_values(o_part, op, "o_part")
+        check_lse(lse_part, sp, "lse_part")
+        check_values(out, o, "o")
+        check_lse(lse, s, "lse")
