@@ -13,10 +13,13 @@ A step runs, on synthetic data resident in HBM:
 Inputs are rotated across copies so that consecutive uses of one buffer are
 separated by far more traffic than the 256 MB Infinity Cache holds.
 
-Output: one JSON line. value = algorithmic HBM bytes of a step / step time
-(GB/s, 1e9). Per-kernel durations come from HIP events recorded on the stream
-the kernels run on; the roofline object describes the kernel that takes the
-most time in a step. cpu_baseline times the fp64 CPU oracle on a bounded
+Output: one JSON line. value = the N-state merge's algorithmic HBM bytes / its
+launch time inside the step (GB/s, 1e9), with frac_of_peak against 8 TB/s;
+decode_us is the split-KV decode at B=1, ctx=32768 (both passes, back to back)
+and the whole step's rate is under "step". Per-kernel durations come from HIP
+events recorded on the stream the kernels run on; the roofline object
+describes the kernel that takes the most time in a step, "rooflines" the two
+kernels of the metric. cpu_baseline times the fp64 CPU oracle on a bounded
 sample of the same inputs.
 """
 from __future__ import annotations
@@ -288,6 +291,7 @@ def build_workload(torch, mi, inputs):
                              f"prefix level on MFMA ({n_ch} chunks), suffix decode "
                              f"(splits={c_splits}) whose combine merges the prefix chunks")))
     host = dict(ms=ms, mss=mss, dec=dec, cas=cas, cascade_bytes=cascade_bytes, splits=splits,
+                mss_call=mss_call, ms_calls=ms_calls,
                 decode_calls=decode_calls,
                 prefix_call=prefix_call, prefix_flops=prefix_flops, prefix_bytes=prefix_bytes,
                 four_launch=[prefix_call, suffix_call, level_merge], cascade_call=cascade_call,
@@ -884,6 +888,8 @@ def main():
         "cascade_prefix_level": loop_us(lambda i: host["prefix_call"](), args.steps),
         "cascade_four_launch": loop_us(lambda i: [c_() for c_ in host["four_launch"]], args.steps),
         "cascade": loop_us(lambda i: host["cascade_call"](), args.steps),
+        "merge_states": loop_us(lambda i: host["mss_call"](), args.steps),
+        "merge_state": loop_us(lambda i: host["ms_calls"][i % 2](), args.steps),
     }
     # The practical read rate in the same run: the plain streaming read over
     # 1 GiB (two buffers rotated), as context for the fractions of the peak.
@@ -897,7 +903,7 @@ def main():
     torch.cuda.empty_cache()
 
     step_bytes = sum(p["bytes"] for p in parts)
-    value = step_bytes / (ms_per_step / 1000.0) / 1e9
+    step_gbs = step_bytes / (ms_per_step / 1000.0) / 1e9
     per = []
     for p in parts:
         us = timer.mean_us(p["name"])
@@ -908,35 +914,54 @@ def main():
             tf = p["flops"] / (us * 1e-6) / 1e12
             entry.update({"TFLOP/s": round(tf, 1), "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)})
         per.append(entry)
+    by_name = {e["kernel"]: e for e in per}
+
+    def roofline_of(entry):
+        return {"bound": "hbm", "achieved": entry["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": entry["frac"], "traffic": counter_traffic(entry["kernel"]),
+                "kernel": entry["kernel"]}
+
+    # The headline: the N-state merge at its streaming size, event-timed per
+    # launch inside the steps; beside it the decode at B=1, ctx=32768.
+    mss = by_name["merge_states"]
     dom = max(per, key=lambda r: r["us"])
-    traffic = counter_traffic(dom["kernel"])
-    roofline = {"bound": "hbm", "achieved": dom["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": dom["frac"], "traffic": traffic, "kernel": dom["kernel"]}
     decode_us = extra["decode"]
-    dec_bytes = [p for p in parts if p["name"] == "split_kv_decode"][0]["bytes"]
+    dec_bytes = by_name["split_kv_decode"]["bytes"]
     line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "metric": METRIC, "value": mss["GB/s"], "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "storage_dtypes": {"merge_states": "f16", "merge_state": "bf16",
+                           "split_kv_decode": "f16", "cascade": "bf16"},
         "data": "synthetic",
-        "config": {"workload": ("merge_state bf16 S=32768 H=32 D=128 + merge_states f16 "
-                                "S=65536 N=4 H=8 D=128 + split-KV decode f16 B=1 ctx=32768 "
-                                f"Hq=32 Hkv=8 D=128 PAGE=16 splits={host['splits']} + cascade "
-                                "bf16 64 x (8192 shared + 512) Hq=32 Hkv=8 D=128"),
+        "config": {"workload": ("value: merge_states f16 S=65536 N=4 H=8 D=128 (10% empty "
+                                "states), per launch inside the step; step: merge_state bf16 "
+                                "S=32768 H=32 D=128 + merge_states + split-KV decode f16 B=1 "
+                                f"ctx=32768 Hq=32 Hkv=8 D=128 PAGE=16 splits={host['splits']} + "
+                                "cascade bf16 64 x (8192 shared + 512) Hq=32 Hkv=8 D=128"),
                    "step_bytes": step_bytes},
-        "frac_of_peak": round(value / HBM_PEAK_GBS, 4),
-        "gpu_ms_per_step": round(gpu_ms_per_step, 4),
+        "frac_of_peak": mss["frac"],
+        "merge_states_us": mss["us"],
         "decode_us": round(decode_us, 2),
         "decode_GBs": round(dec_bytes / (decode_us * 1e-6) / 1e9, 1),
+        "decode_frac": round(dec_bytes / (decode_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "decode_us_in_step": by_name["split_kv_decode"]["us"],
         "decode_two_launch_us": round(extra["decode_two_launch"], 2),
         "decode_pass1_us": round(extra["split_kv_partial"], 2),
         "decode_combine_us": round(extra["combine"], 2),
+        "merge_states_back_to_back_us": round(extra["merge_states"], 2),
+        "merge_state_back_to_back_us": round(extra["merge_state"], 2),
         "cascade_prefix_level_us": round(extra["cascade_prefix_level"], 2),
         "cascade_prefix_level_TFLOPs": round(host["prefix_flops"] / (extra["cascade_prefix_level"] * 1e-6) / 1e12, 1),
         "cascade_four_launch_us": round(extra["cascade_four_launch"], 2),
         "cascade_two_launch_us": round(extra["cascade"], 2),
+        "step": {"bytes": step_bytes, "GB/s": round(step_gbs, 1),
+                 "frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                 "gpu_ms_per_step": round(gpu_ms_per_step, 4)},
         "kernels": per,
-        "roofline": roofline,
+        "roofline": roofline_of(dom),
+        "rooflines": {"merge_states": roofline_of(mss),
+                      "split_kv_decode": roofline_of(by_name["split_kv_decode"])},
         "practical_read": {"kernel": "mi_stream_read", "bytes": 1 << 30,
                            "GB/s": round(read_gbs, 1), "frac": round(read_gbs / HBM_PEAK_GBS, 4),
                            "roofline_achieved_over_it": round(dom["GB/s"] / read_gbs, 4)},

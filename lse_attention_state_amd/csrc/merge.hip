@@ -4,7 +4,8 @@
 // base-2 LSEs s_i, m = max s_i, w_i = 2^(s_i - m), v = sum w_i v_i / sum w_i,
 // s = m + log2(sum w_i). Both kernels are HBM-bound streams: each lane owns one
 // 8-element (16-byte for 16-bit types) chunk of a row, so a row of D = 128 is
-// read by 16 consecutive lanes with fully coalesced 16-byte loads.
+// read by 16 consecutive lanes with fully coalesced 16-byte loads. Inputs are
+// loaded and outputs stored with the non-temporal (streaming) hint.
 //
 // Empty-state handling: incoming s are sanitised (NaN, +inf -> -inf); weights
 // use the max-based guard so that -inf - (-inf) gives weight 0; a state of
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(kBlock) void merge_state_kernel(
       const float tb = (MODE != kSink && wb > 0.0f) ? wb * xb[j] : 0.0f;
       y[j] = (ta + tb) * inv;
     }
-    store8<DTO>(vo, off, y);
+    store8<DTO, true>(vo, off, y);
   }
   // In-place use may alias so with sa/sb: every lane of the row has read them
   // above, and a row's lanes (D <= 512, so at most 64) sit in one wave.
@@ -185,7 +186,7 @@ __global__ __launch_bounds__(kBlock) void merge_states_kernel(
     float y[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) y[j] = acc[j] * inv;
-    store8<DTO>(vo, row * D + d0, y);
+    store8<DTO, true>(vo, row * D + d0, y);
   }
   if (so != nullptr && lane_in_row == 0) so[row] = m + hw_log2(z);
 }
@@ -366,7 +367,7 @@ __global__ __launch_bounds__(kSegThreads) void merge_segments_kernel(
     float y[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) y[j] = acc[j] * inv;
-    store8<DTO>(vo, row * D + d0, y);
+    store8<DTO, true>(vo, row * D + d0, y);
   }
   if (so != nullptr && c == 0) so[row] = m + hw_log2(z);
 }
