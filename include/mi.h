@@ -50,7 +50,8 @@ typedef enum {
   MI_ERR_DTYPE = 3,       /* dtype code out of range or not allowed for this argument */
   MI_ERR_UNSUPPORTED = 4, /* valid but not built: head dim, page size, group size, alignment */
   MI_ERR_HIP = 5,         /* a HIP launch failed */
-  MI_ERR_ALIAS = 6        /* outputs overlap inputs other than by exact in-place aliasing */
+  MI_ERR_ALIAS = 6,       /* outputs overlap inputs other than by exact in-place aliasing */
+  MI_ERR_SCRATCH = 7      /* the work needs more than the library's static scratch holds */
 } mi_status;
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -367,6 +368,28 @@ mi_status mi_cascade_decode(const void* q, const void* k_cache, const void* v_ca
 /* Workspace bytes mi_prefix_attention needs for this shape (host only). */
 mi_status mi_prefix_attention_workspace(int32_t R, int32_t Hq, int32_t Hkv, int32_t D,
                                         int32_t prefix_len, size_t* ws_bytes);
+
+/*
+ * Split-KV paged decode that allocates nothing, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. Same computation, arguments and rules as
+ * mi_split_kv_decode without o_part / lse_part: the fp32 partials live in a
+ * static device array of the library (one per GPU, held until the process
+ * ends) and are not returned. Two launches on `stream` (one with a single
+ * split); nothing is allocated, freed or synchronised.
+ *   B * Hq * num_splits must not exceed MI_NOALLOC_MAX_PARTIAL_ROWS (the array
+ *   holds that many partial rows of D = 128 floats plus their LSEs, about
+ *   16.5 MB); larger work returns MI_ERR_SCRATCH without enqueuing anything.
+ * All calls on one GPU share the array: calls that overlap on one GPU (other
+ * streams, other threads) race on it and must be serialised by the caller.
+ */
+#define MI_NOALLOC_MAX_PARTIAL_ROWS 32768
+mi_status mi_split_kv_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* page_table, int32_t pt_stride,
+                                     const int32_t* ctx_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                                     int32_t D, int32_t page_size, int64_t num_phys_pages,
+                                     int32_t num_splits, float sm_scale, mi_dtype kv_dtype,
+                                     void* o, float* lse, mi_dtype out_dtype, void* stream);
 
 /*
  * Measurement aid, not a step of the method: one plain streaming read of a

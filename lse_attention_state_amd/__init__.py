@@ -24,7 +24,10 @@ MI_F16, MI_BF16, MI_F32 = 0, 1, 2
 _DT = {torch.float16: MI_F16, torch.bfloat16: MI_BF16, torch.float32: MI_F32}
 
 STATUS = {0: "MI_OK", 1: "MI_ERR_NULL", 2: "MI_ERR_SHAPE", 3: "MI_ERR_DTYPE",
-          4: "MI_ERR_UNSUPPORTED", 5: "MI_ERR_HIP", 6: "MI_ERR_ALIAS"}
+          4: "MI_ERR_UNSUPPORTED", 5: "MI_ERR_HIP", 6: "MI_ERR_ALIAS", 7: "MI_ERR_SCRATCH"}
+
+# Largest B * Hq * num_splits that split_kv_decode_noalloc accepts (include/mi.h).
+NOALLOC_MAX_PARTIAL_ROWS = 32768
 
 # (name, argtypes) of every exported entry point; the list mirrors include/mi.h.
 _P, _I32, _I64, _F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
@@ -58,6 +61,8 @@ SIGNATURES = {
                                   _P, _I32, _F, ctypes.c_int, _P, _P, _P, _P, _P, ctypes.c_int,
                                   _P],
     "mi_stream_read": [_P, _I64, _P, _P],
+    "mi_split_kv_decode_noalloc": [_P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I64,
+                                   _I32, _F, ctypes.c_int, _P, _P, ctypes.c_int, _P],
 }
 
 
@@ -488,6 +493,26 @@ def split_kv_decode_varlen(q, k_cache, v_cache, page_table, ctx_lens, split_indp
           _ptr(lse), _dt(out), _stream(q))
     if return_partials:
         return out, lse, o_part, lse_part
+    return out, lse
+
+
+def split_kv_decode_noalloc(q, k_cache, v_cache, page_table, ctx_lens, num_splits: int,
+                            sm_scale: float, out, lse=None):
+    """Two-launch decode whose partials live in the library's static device
+    scratch (the C entry point allocates nothing; ``out`` [B, Hq, D] and the
+    optional ``lse`` [B, Hq] f32 are the caller's) -> (out, lse). Calls that
+    overlap on one GPU race on the scratch."""
+    B, Hq, Hkv, D, page, P = _decode_args(q, k_cache, v_cache, page_table, ctx_lens)
+    if out is None:
+        raise ValueError("split_kv_decode_noalloc: out must be given")
+    _decode_outputs(B, Hq, Hkv, D, (B, Hq, num_splits), None, None, out, lse)
+    if B * Hq * num_splits > NOALLOC_MAX_PARTIAL_ROWS:
+        raise ValueError(f"split_kv_decode_noalloc: B * Hq * num_splits = {B * Hq * num_splits} "
+                         f"exceeds {NOALLOC_MAX_PARTIAL_ROWS}")
+    _check_cuda(q, k_cache, v_cache, page_table, ctx_lens, out, lse)
+    _call("mi_split_kv_decode_noalloc", _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+          page_table.shape[1], _ptr(ctx_lens), B, Hq, Hkv, D, page, P, num_splits,
+          float(sm_scale), _dt(q), _ptr(out), _ptr(lse), _dt(out), _stream(q))
     return out, lse
 
 

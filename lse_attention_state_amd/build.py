@@ -18,7 +18,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libmi.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["abi.cpp", "merge.hip", "decode.hip", "cascade.hip", "measure.hip"]
+SOURCES = ["abi.cpp", "merge.hip", "decode.hip", "cascade.hip", "measure.hip", "noalloc.hip"]
 
 # No fast-math: -inf / NaN semantics are part of the contract. Packed fp32
 # instructions are disabled for device code.

@@ -145,6 +145,9 @@ const char* mi_status_string(mi_status status) {
     case MI_ERR_UNSUPPORTED: return "MI_ERR_UNSUPPORTED: size, dtype or alignment not supported";
     case MI_ERR_HIP: return "MI_ERR_HIP: a HIP call failed";
     case MI_ERR_ALIAS: return "MI_ERR_ALIAS: outputs overlap inputs";
+    case MI_ERR_SCRATCH:
+      return "MI_ERR_SCRATCH: more partial rows than the static scratch holds "
+             "(B * Hq * num_splits > MI_NOALLOC_MAX_PARTIAL_ROWS)";
   }
   return "unknown mi_status";
 }
