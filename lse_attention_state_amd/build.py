@@ -28,6 +28,9 @@ CFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC,
 ]
+# Extra macro definitions, e.g. MI_BUILD_DEFINES="MI_DECODE_STRICT_RELEASE=1"
+# for the single-launch decode's release-ordered counter update.
+CFLAGS += ["-D" + d for d in os.environ.get("MI_BUILD_DEFINES", "").split()]
 
 
 def _compile(src: str) -> str:

@@ -63,6 +63,15 @@ constexpr int kBufferFlags = 0x00020000;
 constexpr int kKvCachePolicy = MI_DECODE_KV_POLICY;
 // s_waitcnt immediate (gfx9 encoding) for vmcnt(0), other counters unconstrained.
 constexpr int kWaitVmcnt0 = 0x0F70;
+// Ordering of the single-launch hand-off's counter update. 0 (default): a
+// relaxed agent-scope add after the write-through partial stores have
+// completed; this relies on how gfx942/gfx950 perform agent-scope stores
+// (written through to the device coherence point, acknowledged only once
+// there). 1: a release add, which the language memory model alone makes
+// sufficient, at the cost of an L2 writeback in every workgroup.
+#ifndef MI_DECODE_STRICT_RELEASE
+#define MI_DECODE_STRICT_RELEASE 0
+#endif
 
 template <int DT>
 __device__ __forceinline__ float dot8acc(const u32x4_t& q, const u32x4_t& k, float acc) {
@@ -796,8 +805,10 @@ __global__ __launch_bounds__(kThreads) void split_kv_partial_kernel(
     if (quarter == 0 && lane == 0) {
       int go = mode == 1 ? 1 : 0;
       if (mode == 2) {
-        const int prev = __hip_atomic_fetch_add(counters + static_cast<int64_t>(b) * Hkv + hkv, 1,
-                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int prev = __hip_atomic_fetch_add(
+            counters + static_cast<int64_t>(b) * Hkv + hkv, 1,
+            MI_DECODE_STRICT_RELEASE ? __ATOMIC_RELEASE : __ATOMIC_RELAXED,
+            __HIP_MEMORY_SCOPE_AGENT);
         go = prev == nsplit - 1 ? 2 : 0;
       }
       lds_go = go;

@@ -4,8 +4,13 @@
 // base-2 LSEs s_i, m = max s_i, w_i = 2^(s_i - m), v = sum w_i v_i / sum w_i,
 // s = m + log2(sum w_i). Both kernels are HBM-bound streams: each lane owns one
 // 8-element (16-byte for 16-bit types) chunk of a row, so a row of D = 128 is
-// read by 16 consecutive lanes with fully coalesced 16-byte loads. Inputs are
-// loaded and outputs stored with the non-temporal (streaming) hint.
+// read by 16 consecutive lanes with fully coalesced 16-byte loads (fp32 rows:
+// a lane's 8 elements are two 4-element pieces, one in each half of the row,
+// so every load instruction of a lane group covers one contiguous run). Every
+// load of a row or batch is issued before the first is used (scheduling
+// barriers keep the compiler from sinking loads toward their uses, which had
+// left one or two in flight). Inputs are loaded and outputs stored with the
+// non-temporal (streaming) hint.
 //
 // Empty-state handling: incoming s are sanitised (NaN, +inf -> -inf); weights
 // use the max-based guard so that -inf - (-inf) gives weight 0; a state of
@@ -22,6 +27,7 @@
 // one-pass layout (section 7's "many index sets" variant).
 #include "common.h"
 #include "launch.h"
+#include <type_traits>
 
 namespace mi {
 namespace {
@@ -34,6 +40,35 @@ int next_pow2(int x) {
   int p = 1;
   while (p < x) p <<= 1;
   return p;
+}
+
+// fp32 rows in two halves: lane c holds elements [4c, 4c + 4) and
+// [D/2 + 4c, D/2 + 4c + 4), so each load instruction of a lane group reads
+// one contiguous run of 16 L bytes (D = 8 L).
+__device__ __forceinline__ void load8_halves(const float* row, int c, int half, float (&x)[8]) {
+  const float4_t a = __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(row + 4 * c));
+  const float4_t b = __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(row + half + 4 * c));
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+template <int DT>
+__device__ __forceinline__ void store8_halves(void* base, int64_t rowoff, int c, int half,
+                                              const float (&x)[8]) {
+  if constexpr (DT == MI_F32) {
+    float* row = static_cast<float*>(base) + rowoff;
+    __builtin_nontemporal_store(float4_t{x[0], x[1], x[2], x[3]}, reinterpret_cast<float4_t*>(row + 4 * c));
+    __builtin_nontemporal_store(float4_t{x[4], x[5], x[6], x[7]}, reinterpret_cast<float4_t*>(row + half + 4 * c));
+  } else {
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    uint16_t* row = static_cast<uint16_t*>(base) + rowoff;
+    const u32x2_t lo = (DT == MI_F16) ? u32x2_t{pack_f16(x[0], x[1]), pack_f16(x[2], x[3])}
+                                      : u32x2_t{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
+    const u32x2_t hi = (DT == MI_F16) ? u32x2_t{pack_f16(x[4], x[5]), pack_f16(x[6], x[7])}
+                                      : u32x2_t{pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])};
+    __builtin_nontemporal_store(lo, reinterpret_cast<u32x2_t*>(row + 4 * c));
+    __builtin_nontemporal_store(hi, reinterpret_cast<u32x2_t*>(row + half + 4 * c));
+  }
 }
 
 // Two states. Lanes per row L = 2^lanes_shift >= D/8; a block covers 256/L rows.
@@ -53,22 +88,29 @@ __global__ __launch_bounds__(kBlock) void merge_state_kernel(
   if constexpr (MODE == kMasked) {
     if (mask[row / H] == 0) return;
   }
-  const float a = sanitize_lse(sa[row]);
-  float b;
+  // All loads of the row are issued before any is used: the state loads do not
+  // wait for the LSE loads. Lanes past D read the row's first chunk (in
+  // bounds) and store nothing.
+  const int d0 = lane_in_row * 8;
+  const int64_t off = row * D + (d0 < D ? d0 : 0);
+  float xa[8], xb[8];
+  load8<DTI>(va, off, xa);
+  if constexpr (MODE != kSink) load8<DTI>(vb, off, xb);
+  const float sa_raw = sa[row];
+  float sb_raw;
   if constexpr (MODE == kSink)
-    b = sanitize_lse(sink[row % H] * kLog2e);
+    sb_raw = sink[row % H] * kLog2e;
   else
-    b = sanitize_lse(sb[row]);
+    sb_raw = sb[row];
+  __builtin_amdgcn_sched_barrier(0);
+  const float a = sanitize_lse(sa_raw);
+  const float b = sanitize_lse(sb_raw);
   const float m = __builtin_fmaxf(a, b);
   const float wa = guarded_exp2(a - m);
   const float wb = guarded_exp2(b - m);
   const float z = wa + wb;
-  const int d0 = lane_in_row * 8;
   if (d0 < D) {
-    const int64_t off = row * D + d0;
-    float xa[8], xb[8], y[8];
-    load8<DTI>(va, off, xa);
-    if constexpr (MODE != kSink) load8<DTI>(vb, off, xb);
+    float y[8];
     const float inv = guarded_inv(z);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -84,11 +126,12 @@ __global__ __launch_bounds__(kBlock) void merge_state_kernel(
   if (so != nullptr && lane_in_row == 0) so[row] = m + hw_log2(z);
 }
 
+
 // N states. Each row (pos, h) is served by G = 2^groups_shift groups of L lanes;
 // group g handles states n = g, g+G, ...; groups are merged through LDS.
 constexpr int kLdsFloats = 2048 + 512;  // rows_per_block * G * (8L + 2) <= 2048 + 512/L
 
-template <int DTI, int DTO, int kChunk>
+template <int DTI, int DTO, int kChunk, bool kHalves = false>
 __global__ __launch_bounds__(kBlock) void merge_states_kernel(
     const void* __restrict__ v, const float* __restrict__ s, void* __restrict__ vo,
     float* __restrict__ so, int64_t rows, int N, int H, int D, int lanes_shift,
@@ -127,8 +170,12 @@ __global__ __launch_bounds__(kBlock) void merge_states_kernel(
         const int n = n0 + u * G;
         const int64_t idx = (pos * N + (n < N ? n : 0)) * H + h;
         sv[u] = s[idx];
-        load8<DTI>(v, idx * D + (lane_ok ? d0 : 0), x[u]);
+        if constexpr (kHalves)
+          load8_halves(static_cast<const float*>(v) + idx * D, lane_in_row, D / 2, x[u]);
+        else
+          load8<DTI>(v, idx * D + (lane_ok ? d0 : 0), x[u]);
       }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < kChunk; ++u) {
         const bool in = n0 + u * G < N;
@@ -186,7 +233,10 @@ __global__ __launch_bounds__(kBlock) void merge_states_kernel(
     float y[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) y[j] = acc[j] * inv;
-    store8<DTO, true>(vo, row * D + d0, y);
+    if constexpr (kHalves)
+      store8_halves<DTO>(vo, row * D, lane_in_row, D / 2, y);
+    else
+      store8<DTO, true>(vo, row * D + d0, y);
   }
   if (so != nullptr && lane_in_row == 0) so[row] = m + hw_log2(z);
 }
@@ -224,6 +274,7 @@ hipError_t merge_state_mode(const void* va, const float* sa, const void* vb, con
   }
 }
 
+
 // Segmented merge: row (pos, h) merges the states start..end-1 of v [total, H, D],
 // s [total, H], where [start, end) = [indptr[pos], indptr[pos+1]) clamped to
 // [0, total], or [pos*N, (pos+1)*N) when indptr is null (the N-state layout
@@ -242,7 +293,7 @@ constexpr int kSegMaxD = 512;
 // parts > 1 (no indptr): each position's N states are cut into `parts`
 // consecutive slices of ceil(N / parts), and row (pos * parts + part) * H + h
 // merges one slice -- the first level of a two-level merge.
-template <int DTI, int DTO, int K, int kSegThreads>
+template <int DTI, int DTO, int K, int kSegThreads, bool kHalves = false>
 __global__ __launch_bounds__(kSegThreads) void merge_segments_kernel(
     const void* __restrict__ v, const float* __restrict__ s, const int32_t* __restrict__ indptr,
     int64_t total, int N, void* __restrict__ vo, float* __restrict__ so, int64_t rows, int H,
@@ -286,20 +337,30 @@ __global__ __launch_bounds__(kSegThreads) void merge_segments_kernel(
   float m = -kInf, z = 0.0f, acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-  for (int64_t k0 = g; k0 < n; k0 += static_cast<int64_t>(G) * K) {
-    float sv[K], x[K][8];
-    // Unconditional loads at clamped indices, selected afterwards (a masked
-    // load followed by a zero-fill would wait after every load).
+  // States are folded in batches of KK per lane (KK <= K), all of a batch's
+  // loads in flight together. The batch size is the smallest power of two
+  // that covers what the wave's lanes still have, so short sets issue no
+  // loads for states they do not have. Lanes whose set is done (or empty)
+  // take part with every state masked; their loads use an index that exists
+  // (the set's first state, or state 0 of the array for an empty set: some
+  // lane of the wave still has states, so the arrays are not empty).
+  auto fold = [&](auto kk, int64_t k0) {
+    constexpr int KK = decltype(kk)::value;
+    float sv[KK], x[KK][8];
 #pragma unroll
-    for (int u = 0; u < K; ++u) {
+    for (int u = 0; u < KK; ++u) {
       const int64_t k = k0 + static_cast<int64_t>(u) * G;
-      const int64_t idx = (start + (k < n ? k : 0)) * H + h;
+      const int64_t idx = (k < n ? start + k : (n > 0 ? start : 0)) * H + h;
       sv[u] = s[idx];
-      load8<DTI>(v, idx * D + (lane_ok ? d0 : 0), x[u]);
+      if constexpr (kHalves)
+        load8_halves(static_cast<const float*>(v) + idx * D, c, D / 2, x[u]);
+      else
+        load8<DTI>(v, idx * D + (lane_ok ? d0 : 0), x[u]);
     }
+    __builtin_amdgcn_sched_barrier(0);
     float cm = m;
 #pragma unroll
-    for (int u = 0; u < K; ++u) {
+    for (int u = 0; u < KK; ++u) {
       sv[u] = (k0 + static_cast<int64_t>(u) * G < n) ? sanitize_lse(sv[u]) : -kInf;
       cm = __builtin_fmaxf(cm, sv[u]);
     }
@@ -308,7 +369,7 @@ __global__ __launch_bounds__(kSegThreads) void merge_segments_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] *= keep;
 #pragma unroll
-    for (int u = 0; u < K; ++u) {
+    for (int u = 0; u < KK; ++u) {
       const float w = guarded_exp2(sv[u] - cm);
       z += w;
 #pragma unroll
@@ -316,6 +377,24 @@ __global__ __launch_bounds__(kSegThreads) void merge_segments_kernel(
         acc[j] = (w > 0.0f && lane_ok) ? __builtin_fmaf(w, x[u][j], acc[j]) : acc[j];
     }
     m = cm;
+  };
+  for (int64_t k0 = g;;) {
+    const int64_t rem = n - k0;
+    if (K >= 8 && __builtin_amdgcn_ballot_w64(rem > 4 * static_cast<int64_t>(G)) != 0) {
+      fold(std::integral_constant<int, (K >= 8 ? 8 : 1)>{}, k0);
+      k0 += 8 * static_cast<int64_t>(G);
+    } else if (K >= 4 && __builtin_amdgcn_ballot_w64(rem > 2 * static_cast<int64_t>(G)) != 0) {
+      fold(std::integral_constant<int, (K >= 4 ? 4 : 1)>{}, k0);
+      k0 += 4 * static_cast<int64_t>(G);
+    } else if (K >= 2 && __builtin_amdgcn_ballot_w64(rem > static_cast<int64_t>(G)) != 0) {
+      fold(std::integral_constant<int, (K >= 2 ? 2 : 1)>{}, k0);
+      k0 += 2 * static_cast<int64_t>(G);
+    } else if (__builtin_amdgcn_ballot_w64(rem > 0) != 0) {
+      fold(std::integral_constant<int, 1>{}, k0);
+      k0 += static_cast<int64_t>(G);
+    } else {
+      break;
+    }
   }
   // Merge the lane groups inside each wave (lanes c, c + L, c + 2L, ... of the team).
   const int in_wave = T < 64 ? T : 64;
@@ -367,28 +446,31 @@ __global__ __launch_bounds__(kSegThreads) void merge_segments_kernel(
     float y[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) y[j] = acc[j] * inv;
-    store8<DTO, true>(vo, row * D + d0, y);
+    if constexpr (kHalves)
+      store8_halves<DTO>(vo, row * D, c, D / 2, y);
+    else
+      store8<DTO, true>(vo, row * D + d0, y);
   }
   if (so != nullptr && c == 0) so[row] = m + hw_log2(z);
 }
 
-template <int DTI, int DTO, int kThr>
+template <int DTI, int DTO, int kThr, bool kH = false>
 hipError_t merge_segments_kt(int K, dim3 grid, hipStream_t st, const void* v, const float* s,
                              const int32_t* indptr, int64_t total, int N, void* vo, float* so,
                              int64_t rows, int H, int D, int lanes_shift, int team_shift,
                              int parts) {
   switch (K) {
     case 1:
-      merge_segments_kernel<DTI, DTO, 1, kThr><<<grid, kThr, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts);
+      merge_segments_kernel<DTI, DTO, 1, kThr, kH><<<grid, kThr, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts);
       break;
     case 2:
-      merge_segments_kernel<DTI, DTO, 2, kThr><<<grid, kThr, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts);
+      merge_segments_kernel<DTI, DTO, 2, kThr, kH><<<grid, kThr, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts);
       break;
     case 4:
-      merge_segments_kernel<DTI, DTO, 4, kThr><<<grid, kThr, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts);
+      merge_segments_kernel<DTI, DTO, 4, kThr, kH><<<grid, kThr, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts);
       break;
     default:
-      merge_segments_kernel<DTI, DTO, 8, kThr><<<grid, kThr, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts);
+      merge_segments_kernel<DTI, DTO, 8, kThr, kH><<<grid, kThr, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts);
       break;
   }
   return hipGetLastError();
@@ -402,6 +484,13 @@ hipError_t merge_segments_k(int K, int64_t rows, hipStream_t st, const void* v, 
   const int threads = team_shift > 8 ? 1024 : 256;
   const int64_t rows_per_block = threads >> team_shift;
   const dim3 grid(static_cast<unsigned>((rows + rows_per_block - 1) / rows_per_block));
+  if constexpr (DTI == MI_F32) {
+    if (D == (8 << lanes_shift)) {
+      if (threads == 1024)
+        return merge_segments_kt<DTI, DTO, 1024, true>(K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts);
+      return merge_segments_kt<DTI, DTO, 256, true>(K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts);
+    }
+  }
   if (threads == 1024)
     return merge_segments_kt<DTI, DTO, 1024>(K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts);
   return merge_segments_kt<DTI, DTO, 256>(K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts);
@@ -422,38 +511,38 @@ hipError_t merge_segments_out(int dt_out, int K, int64_t rows, hipStream_t st, c
   }
 }
 
-template <int DTI, int DTO>
+template <int DTI, int DTO, bool kH>
 hipError_t merge_states_chunk(int chunk, const void* v, const float* s, void* vo, float* so,
                               int64_t rows, int N, int H, int D, int lanes_shift,
                               int groups_shift, dim3 grid, hipStream_t st) {
   switch (chunk) {
     case 1:
-      merge_states_kernel<DTI, DTO, 1><<<grid, kBlock, 0, st>>>(v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift);
+      merge_states_kernel<DTI, DTO, 1, kH><<<grid, kBlock, 0, st>>>(v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift);
       break;
     case 2:
-      merge_states_kernel<DTI, DTO, 2><<<grid, kBlock, 0, st>>>(v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift);
+      merge_states_kernel<DTI, DTO, 2, kH><<<grid, kBlock, 0, st>>>(v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift);
       break;
     case 4:
-      merge_states_kernel<DTI, DTO, 4><<<grid, kBlock, 0, st>>>(v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift);
+      merge_states_kernel<DTI, DTO, 4, kH><<<grid, kBlock, 0, st>>>(v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift);
       break;
     default:
-      merge_states_kernel<DTI, DTO, 8><<<grid, kBlock, 0, st>>>(v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift);
+      merge_states_kernel<DTI, DTO, 8, kH><<<grid, kBlock, 0, st>>>(v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift);
       break;
   }
   return hipGetLastError();
 }
 
-template <int DTI>
+template <int DTI, bool kH = false>
 hipError_t merge_states_out(int dt_out, int chunk, const void* v, const float* s, void* vo,
                             float* so, int64_t rows, int N, int H, int D, int lanes_shift,
                             int groups_shift, dim3 grid, hipStream_t st) {
   switch (dt_out) {
     case MI_F16:
-      return merge_states_chunk<DTI, MI_F16>(chunk, v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift, grid, st);
+      return merge_states_chunk<DTI, MI_F16, kH>(chunk, v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift, grid, st);
     case MI_BF16:
-      return merge_states_chunk<DTI, MI_BF16>(chunk, v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift, grid, st);
+      return merge_states_chunk<DTI, MI_BF16, kH>(chunk, v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift, grid, st);
     default:
-      return merge_states_chunk<DTI, MI_F32>(chunk, v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift, grid, st);
+      return merge_states_chunk<DTI, MI_F32, kH>(chunk, v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift, grid, st);
   }
 }
 
@@ -563,7 +652,11 @@ hipError_t launch_merge_states(const void* v, const float* s, void* vo, float* s
   switch (dt_in) {
     case MI_F16: return merge_states_out<MI_F16>(dt_out, chunk, v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift, grid, st);
     case MI_BF16: return merge_states_out<MI_BF16>(dt_out, chunk, v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift, grid, st);
-    default: return merge_states_out<MI_F32>(dt_out, chunk, v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift, grid, st);
+    default:
+      // fp32 rows in halves (whole-row runs per load instruction) when D = 8 L.
+      if (D == (8 << lanes_shift))
+        return merge_states_out<MI_F32, true>(dt_out, chunk, v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift, grid, st);
+      return merge_states_out<MI_F32>(dt_out, chunk, v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift, grid, st);
   }
 }
 
