@@ -431,9 +431,10 @@ def sweep(torch, mi, inputs, iters, with_cpu=True):
     # against mi_merge_states_varlen (always the segmented kernel) on the same data.
     out += ["", "| merge | shape | mi_merge_states µs | mi_merge_states_varlen µs | "
             "mi_merge_states_two_level µs |", "|---|---|---:|---:|---:|"]
+    two_level_rows = []
     for S, N, H, dt in ((32, 64, 1, "f32"), (1024, 16, 1, "f32"), (2048, 16, 1, "f32"),
                         (4096, 16, 1, "f32"), (4096, 4, 8, "f16"), (512, 64, 8, "f16"),
-                        (64, 1024, 1, "f32")):
+                        (64, 1024, 1, "f32"), (64, 16384, 1, "f32")):
         c = inputs.merge_states_case(2100 + N, S=S, N=N, H=H, D=D, dtype=dt)
         cop = [(to_dev(c["v"], dt, torch), torch.from_numpy(c["s"]).cuda()) for _ in range(4)]
         vo = torch.empty((S, H, D), dtype=torch.float16, device="cuda")
@@ -453,6 +454,11 @@ def sweep(torch, mi, inputs, iters, with_cpu=True):
         tw = _loop_us(torch, lambda i: w[i % 4](), iters)
         out.append(f"| merge_states {dt}->f16 | S={S} N={N} H={H} D={D} | {ta:.1f} | {tb:.1f} | "
                    f"{tw:.1f} |")
+        if N >= 1024:
+            by = S * N * H * (D * 4 + 4) + S * H * (D * 2 + 4)
+            two_level_rows.append(
+                f"| merge_states_two_level (two launches) | f32->f16 S={S} N={N} H={H} D={D} | "
+                f"{tw:.1f} | {by} | {by / (tw * 1e-6) / 1e9:.0f} | {by / (tw * 1e-6) / 8e12 * 100:.1f} |")
         del cop
         torch.cuda.empty_cache()
 
@@ -506,21 +512,28 @@ def sweep(torch, mi, inputs, iters, with_cpu=True):
         by = int(rows_ * frac) * (3 * 256 + 3 * 4) + 32768
         out.append(f"| merge_state_in_place, mask {label} | bf16 S=32768 H=32 D=128 | {t:.1f} | "
                    f"{by} | {by / (t * 1e-6) / 1e9:.0f} | {by / (t * 1e-6) / 8e12 * 100:.1f} |")
-    # Variable-length merge at a streaming size: 8192 sets of 0..8 fp16 states, H=8.
-    indptr = inputs.segment_indptr(2200, 8192, 8)
-    total = int(indptr[-1])
-    c = inputs.merge_states_case(2201, S=1, N=total, H=8, D=128, dtype="f16")
-    vv = [to_dev(c["v"].reshape(total, 8, 128), "f16", torch) for _ in range(4)]
-    ss = torch.from_numpy(c["s"].reshape(total, 8)).cuda()
-    ipd = torch.from_numpy(indptr).cuda()
-    vo = torch.empty((8192, 8, 128), dtype=torch.float16, device="cuda")
-    so = torch.empty((8192, 8), dtype=torch.float32, device="cuda")
-    calls = [Raw(mi, "mi_merge_states_varlen", vv[i], ss, ipd, total, vo, so, 8192, 8, 128,
-                 mi.MI_F16, mi.MI_F16, st) for i in range(4)]
-    t = _loop_us(torch, lambda i: calls[i % 4](), iters)
-    by = total * 8 * (256 + 4) + 8193 * 4 + 8192 * 8 * (256 + 4)
-    out.append(f"| merge_states_varlen | f16 8192 sets x U[0..8] states ({total}), H=8 D=128 | "
-               f"{t:.1f} | {by} | {by / (t * 1e-6) / 1e9:.0f} | {by / (t * 1e-6) / 8e12 * 100:.1f} |")
+    # Variable-length merges: 8192 and 65536 sets of 0..8 fp16 states, H=8.
+    for n_sets, seeds in ((65536, (2202, 2203)), (8192, (2200, 2201))):
+        indptr_ = inputs.segment_indptr(seeds[0], n_sets, 8)
+        total = int(indptr_[-1])
+        c_ = inputs.merge_states_case(seeds[1], S=1, N=total, H=8, D=128, dtype="f16")
+        ncp = 4 if n_sets <= 8192 else 2
+        vv = [to_dev(c_["v"].reshape(total, 8, 128), "f16", torch) for _ in range(ncp)]
+        ss = torch.from_numpy(c_["s"].reshape(total, 8)).cuda()
+        ipd = torch.from_numpy(indptr_).cuda()
+        vo = torch.empty((n_sets, 8, 128), dtype=torch.float16, device="cuda")
+        so = torch.empty((n_sets, 8), dtype=torch.float32, device="cuda")
+        calls = [Raw(mi, "mi_merge_states_varlen", vv[i], ss, ipd, total, vo, so, n_sets, 8, 128,
+                     mi.MI_F16, mi.MI_F16, st) for i in range(ncp)]
+        t = _loop_us(torch, lambda i: calls[i % ncp](), iters)
+        by = total * 8 * (256 + 4) + (n_sets + 1) * 4 + n_sets * 8 * (256 + 4)
+        out.append(f"| merge_states_varlen | f16 {n_sets} sets x U[0..8] states ({total}), H=8 D=128 | "
+                   f"{t:.1f} | {by} | {by / (t * 1e-6) / 1e9:.0f} | {by / (t * 1e-6) / 8e12 * 100:.1f} |")
+        if n_sets == 8192:
+            indptr, c = indptr_, c_
+        del vv, ss, vo, so, calls
+        torch.cuda.empty_cache()
+    out += two_level_rows
     if with_cpu:
         import oracle
         out += [""] + cpu_baseline_sweep(oracle, inputs, ms, sink.cpu().numpy(), indptr, c)
