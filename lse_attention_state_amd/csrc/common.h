@@ -101,6 +101,53 @@ __device__ __forceinline__ void load8(const void* base, int64_t off, float (&x)[
   }
 }
 
+// The same load in two steps: the raw words (two 16-byte loads for fp32, one
+// for 16-bit types), then their conversion to fp32. Kernels that keep many
+// loads in flight issue all raw loads, place a scheduling barrier, and only
+// then convert, so no conversion is scheduled between the loads (which would
+// make the wave wait for one of them early).
+struct Raw8 {
+  u32x4_t a, b;
+};
+
+template <int DT>
+__device__ __forceinline__ Raw8 load8_raw(const void* base, int64_t off) {
+  Raw8 r;
+  if constexpr (DT == MI_F32) {
+    const u32x4_t* p = reinterpret_cast<const u32x4_t*>(static_cast<const float*>(base) + off);
+    r.a = __builtin_nontemporal_load(p);
+    r.b = __builtin_nontemporal_load(p + 1);
+  } else {
+    r.a = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(base) + off));
+    r.b = u32x4_t{0, 0, 0, 0};
+  }
+  return r;
+}
+
+template <int DT>
+__device__ __forceinline__ void unpack8_raw(const Raw8& r, float (&x)[8]) {
+  if constexpr (DT == MI_F32) {
+    // Cast whole vectors: a bit_cast of a single ext-vector element has been
+    // compiled as a read of element 0.
+    const float4_t fa = __builtin_bit_cast(float4_t, r.a);
+    const float4_t fb = __builtin_bit_cast(float4_t, r.b);
+    x[0] = fa.x; x[1] = fa.y; x[2] = fa.z; x[3] = fa.w;
+    x[4] = fb.x; x[5] = fb.y; x[6] = fb.z; x[7] = fb.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (DT == MI_F16) {
+        x[2 * i] = f16_lo(r.a[i]);
+        x[2 * i + 1] = f16_hi(r.a[i]);
+      } else {
+        x[2 * i] = bf16_lo(r.a[i]);
+        x[2 * i + 1] = bf16_hi(r.a[i]);
+      }
+    }
+  }
+}
+
 // Store of 8 elements rounded to DT. kStream: with the non-temporal hint, for
 // outputs a streaming merge writes once and does not read back (measured on
 // MI355X: the merges' dirty output no longer lingers in the last-level cache

@@ -45,11 +45,13 @@ int next_pow2(int x) {
 // fp32 rows in two halves: lane c holds elements [4c, 4c + 4) and
 // [D/2 + 4c, D/2 + 4c + 4), so each load instruction of a lane group reads
 // one contiguous run of 16 L bytes (D = 8 L).
-__device__ __forceinline__ void load8_halves(const float* row, int c, int half, float (&x)[8]) {
-  const float4_t a = __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(row + 4 * c));
-  const float4_t b = __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(row + half + 4 * c));
-  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+// Raw words as for load8_raw<MI_F32>; unpack8_raw<MI_F32> gives the lane's
+// elements in the order [4c, 4c + 4) then [D/2 + 4c, D/2 + 4c + 4).
+__device__ __forceinline__ Raw8 load8_halves_raw(const float* row, int c, int half) {
+  Raw8 r;
+  r.a = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + 4 * c));
+  r.b = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + half + 4 * c));
+  return r;
 }
 
 template <int DT>
@@ -93,9 +95,9 @@ __global__ __launch_bounds__(kBlock) void merge_state_kernel(
   // bounds) and store nothing.
   const int d0 = lane_in_row * 8;
   const int64_t off = row * D + (d0 < D ? d0 : 0);
-  float xa[8], xb[8];
-  load8<DTI>(va, off, xa);
-  if constexpr (MODE != kSink) load8<DTI>(vb, off, xb);
+  const Raw8 ra = load8_raw<DTI>(va, off);
+  Raw8 rb;
+  if constexpr (MODE != kSink) rb = load8_raw<DTI>(vb, off);
   const float sa_raw = sa[row];
   float sb_raw;
   if constexpr (MODE == kSink)
@@ -103,6 +105,9 @@ __global__ __launch_bounds__(kBlock) void merge_state_kernel(
   else
     sb_raw = sb[row];
   __builtin_amdgcn_sched_barrier(0);
+  float xa[8], xb[8];
+  unpack8_raw<DTI>(ra, xa);
+  if constexpr (MODE != kSink) unpack8_raw<DTI>(rb, xb);
   const float a = sanitize_lse(sa_raw);
   const float b = sanitize_lse(sb_raw);
   const float m = __builtin_fmaxf(a, b);
@@ -161,7 +166,7 @@ __global__ __launch_bounds__(kBlock) void merge_states_kernel(
   if (row_ok) {
     for (int n0 = g; n0 < N; n0 += kChunk * G) {
       float sv[kChunk];
-      float x[kChunk][8];
+      Raw8 xr[kChunk];
       // Loads are unconditional (indices clamped to valid ones) and results
       // are selected afterwards: a load under a lane mask followed by a
       // zero-fill of the same registers would force a wait after every load.
@@ -171,11 +176,14 @@ __global__ __launch_bounds__(kBlock) void merge_states_kernel(
         const int64_t idx = (pos * N + (n < N ? n : 0)) * H + h;
         sv[u] = s[idx];
         if constexpr (kHalves)
-          load8_halves(static_cast<const float*>(v) + idx * D, lane_in_row, D / 2, x[u]);
+          xr[u] = load8_halves_raw(static_cast<const float*>(v) + idx * D, lane_in_row, D / 2);
         else
-          load8<DTI>(v, idx * D + (lane_ok ? d0 : 0), x[u]);
+          xr[u] = load8_raw<DTI>(v, idx * D + (lane_ok ? d0 : 0));
       }
       __builtin_amdgcn_sched_barrier(0);
+      float x[kChunk][8];
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) unpack8_raw<DTI>(xr[u], x[u]);
 #pragma unroll
       for (int u = 0; u < kChunk; ++u) {
         const bool in = n0 + u * G < N;
@@ -346,18 +354,22 @@ __global__ __launch_bounds__(kSegThreads) void merge_segments_kernel(
   // lane of the wave still has states, so the arrays are not empty).
   auto fold = [&](auto kk, int64_t k0) {
     constexpr int KK = decltype(kk)::value;
-    float sv[KK], x[KK][8];
+    float sv[KK];
+    Raw8 xr[KK];
 #pragma unroll
     for (int u = 0; u < KK; ++u) {
       const int64_t k = k0 + static_cast<int64_t>(u) * G;
       const int64_t idx = (k < n ? start + k : (n > 0 ? start : 0)) * H + h;
       sv[u] = s[idx];
       if constexpr (kHalves)
-        load8_halves(static_cast<const float*>(v) + idx * D, c, D / 2, x[u]);
+        xr[u] = load8_halves_raw(static_cast<const float*>(v) + idx * D, c, D / 2);
       else
-        load8<DTI>(v, idx * D + (lane_ok ? d0 : 0), x[u]);
+        xr[u] = load8_raw<DTI>(v, idx * D + (lane_ok ? d0 : 0));
     }
     __builtin_amdgcn_sched_barrier(0);
+    float x[KK][8];
+#pragma unroll
+    for (int u = 0; u < KK; ++u) unpack8_raw<DTI>(xr[u], x[u]);
     float cm = m;
 #pragma unroll
     for (int u = 0; u < KK; ++u) {
