@@ -421,3 +421,39 @@ def test_merge_states_two_level(S, N, H, dt):
     rv, rs = oracle.merge_states(c["v"], c["s"], dt)
     check_values(vo, rv)
     check_lse(so, rs)
+
+
+def test_merge_states_two_level_streaming_size():
+    """The sweep's streaming size: fp32 S=64, N=16384, H=1 (32 slices of 512 states,
+    teams of 256 lanes over several batches), every row against the oracle."""
+    _say("two-level merge, streaming size")
+    S, N = 64, 16384
+    c = inputs.merge_states_case(2100 + N, S=S, N=N, H=1, D=128, dtype="f32")
+    need = mi.merge_states_workspace_bytes(S, N, 1, 128)
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    vo, so = mi.merge_states_two_level(torch.from_numpy(c["v"]).cuda(),
+                                       torch.from_numpy(c["s"]).cuda(),
+                                       out_dtype=torch.float16, workspace=ws)
+    torch.cuda.synchronize()
+    rv, rs = oracle.merge_states(c["v"], c["s"], "f32")
+    check_values(vo, rv)
+    check_lse(so, rs)
+
+
+def test_merge_states_varlen_streaming_size():
+    """The sweep's streaming size: 65536 sets of U[0..8] fp16 states, H=8 (adaptive
+    batches in waves whose rows share one set), every row against the oracle."""
+    _say("varlen merge, streaming size")
+    indptr = inputs.segment_indptr(2202, 65536, 8)
+    total = int(indptr[-1])
+    c = inputs.merge_states_case(2203, S=1, N=total, H=8, D=128, dtype="f16")
+    v = np.ascontiguousarray(c["v"].reshape(total, 8, 128))
+    s = np.ascontiguousarray(c["s"].reshape(total, 8))
+    vo = torch.full((65536, 8, 128), float("nan"), dtype=torch.float16, device="cuda")
+    so = torch.full((65536, 8), float("nan"), dtype=torch.float32, device="cuda")
+    mi.merge_states_varlen(to_device(v, "f16"), torch.from_numpy(s).cuda(),
+                           torch.from_numpy(indptr).cuda(), v_out=vo, s_out=so)
+    torch.cuda.synchronize()
+    rv, rs = oracle.merge_states_varlen(v, s, indptr, "f16")
+    check_values(vo, rv)
+    check_lse(so, rs)
