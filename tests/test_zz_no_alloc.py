@@ -64,3 +64,43 @@ def test_noalloc_decode_refuses_work_beyond_the_scratch():
     assert rc == 7   # MI_ERR_SCRATCH
     with pytest.raises(ValueError):
         mi.split_kv_decode_noalloc(q, k, v, pt, cl, splits, case["sm_scale"], out)
+
+
+def test_noalloc_decode_under_graph_capture():
+    """Graph capture is one of the uses this entry point is for: one call is
+    captured, then replayed with new queries copied into the captured buffers
+    (eager work in between); every replay equals the two-launch decode with
+    workspaces on the same inputs, bit for bit."""
+    ctx = np.array([700, 33, 4096], np.int32)
+    case = inputs.paged_kv_case(960, ctx, 32, 8, 128, 16, dtype="f16")
+    q, k, v, pt, cl = _dev(case)
+    splits = 8
+    out = torch.empty((3, 32, 128), dtype=torch.float16, device="cuda")
+    lse = torch.empty((3, 32), dtype=torch.float32, device="cuda")
+
+    def work():
+        mi.split_kv_decode_noalloc(q, k, v, pt, cl, splits, case["sm_scale"], out, lse)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        work()                                     # first call on the device: outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        work()
+    torch.cuda.synchronize()
+    g = torch.Generator(device="cpu").manual_seed(961)
+    for rep in range(3):
+        print("noalloc graph replay", rep, flush=True)
+        q.copy_(torch.randn(q.shape, generator=g).half().cuda())
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got_o, got_s = out.clone(), lse.clone()
+        _ = (torch.randn(1024, device="cuda") * 2).sum()
+        o_ref, s_ref = mi.split_kv_decode(q, k, v, pt, cl, splits, case["sm_scale"])
+        torch.cuda.synchronize()
+        assert torch.equal(got_o.view(torch.int16), o_ref.view(torch.int16))
+        assert torch.equal(got_s.view(torch.int32), s_ref.view(torch.int32))
