@@ -595,16 +595,22 @@ hipError_t launch_merge_segments(const void* v, const float* s, const int32_t* i
   // workgroups per compute unit keep its memory pipeline busy while one of
   // them merges: measured on MI355X, S*H = 2048 slices of 512 fp32 states in
   // 87 us against 107 us with teams of 1024); more lane groups (up to 16
-  // waves per row, while each group keeps at least one state) when there are
-  // too few rows to give the device about 16 waves per compute unit.
+  // waves per row, while each group keeps at least 4 states) when there are
+  // too few rows to give the device about 16 waves per compute unit. (At one
+  // state per group the cross-group merge outweighed the extra loads in
+  // flight: the split combine of 32 rows x 64 fp32 partials took 5.2 us per
+  // call against 4.0 us with 4 states per group.)
   const int64_t avg = indptr != nullptr ? (S > 0 ? (total + S - 1) / S : 0)
                                         : (static_cast<int64_t>(N) + parts - 1) / parts;
   constexpr int64_t kTargetLanes = 4096 * 64;
+  constexpr int kMinStatesPerGroup = 4;
   const int max_groups = 1024 / L;
   const int batch_groups = 256 / L < max_groups ? 256 / L : max_groups;
   int G = 1;
   while (G < batch_groups && static_cast<int64_t>(G) * 8 < avg) G *= 2;
-  while (G < max_groups && 2 * G <= avg && rows * L * G < kTargetLanes) G *= 2;
+  while (G < max_groups && static_cast<int64_t>(2 * G) * kMinStatesPerGroup <= avg &&
+         rows * L * G < kTargetLanes)
+    G *= 2;
   const int team_shift = log2_int(L * G);
   const int64_t per_lane = (avg + G - 1) / G;
   const int K = per_lane >= 8 ? 8 : next_pow2(static_cast<int>(per_lane > 0 ? per_lane : 1));
