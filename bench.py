@@ -566,6 +566,17 @@ def ceiling(torch, mi, iters):
     print(json.dumps({"kernel": "torch device copy: 1 GiB read + 1 GiB written", "bytes": moved,
                       "us": round(t, 2), "GB/s": round(moved / (t * 1e-6) / 1e9, 1),
                       "frac_of_8TBs": round(moved / (t * 1e-6) / 8e12, 4)}))
+    del a, b
+    # The two-state merge's read:write mix (2:1) in a plain elementwise kernel:
+    # torch's add of two bf16 tensors of 256 MiB into a third, inputs rotated.
+    n = 1 << 27
+    xs = [torch.ones(n, dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+    y = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    t = _loop_us(torch, lambda i: torch.add(xs[(2 * i) % 4], xs[(2 * i + 1) % 4], out=y), iters)
+    moved = 3 * n * 2
+    print(json.dumps({"kernel": "torch add, two 256 MiB bf16 inputs into a third (2:1 read:write)",
+                      "bytes": moved, "us": round(t, 2), "GB/s": round(moved / (t * 1e-6) / 1e9, 1),
+                      "frac_of_8TBs": round(moved / (t * 1e-6) / 8e12, 4)}))
 
 
 def cpu_baseline_sweep(oracle, inputs, ms, sink, indptr, vs_case):
