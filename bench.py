@@ -577,6 +577,17 @@ def ceiling(torch, mi, iters):
     print(json.dumps({"kernel": "torch add, two 256 MiB bf16 inputs into a third (2:1 read:write)",
                       "bytes": moved, "us": round(t, 2), "GB/s": round(moved / (t * 1e-6) / 1e9, 1),
                       "frac_of_8TBs": round(moved / (t * 1e-6) / 8e12, 4)}))
+    del xs, y
+    # The N-state merge's mix at N = 4 (4:1): torch's sum over the first axis of a
+    # [4, n] fp16 tensor (four 128 MiB rows into one), inputs rotated.
+    n = 1 << 26
+    xs = [torch.ones((4, n), dtype=torch.float16, device="cuda") for _ in range(2)]
+    y = torch.empty(n, dtype=torch.float16, device="cuda")
+    t = _loop_us(torch, lambda i: torch.sum(xs[i % 2], dim=0, out=y), iters)
+    moved = 5 * n * 2
+    print(json.dumps({"kernel": "torch sum over 4 rows of 128 MiB fp16 into one (4:1 read:write)",
+                      "bytes": moved, "us": round(t, 2), "GB/s": round(moved / (t * 1e-6) / 1e9, 1),
+                      "frac_of_8TBs": round(moved / (t * 1e-6) / 8e12, 4)}))
 
 
 def cpu_baseline_sweep(oracle, inputs, ms, sink, indptr, vs_case):
