@@ -724,6 +724,18 @@ def configs_report(torch, mi, inputs, iters, with_cpu):
     emit("merge_states", "f16 S=64 N=4 H=8 D=128 (10% empty states)", 1001,
          64 * 8 * (4 * 256 + 16 + 256 + 4), ts, {}, cmp1 if oracle else None)
 
+    # The per-call floor of this timing: one near-empty launch (a 4 KiB plain
+    # read), for scale beside the small workload above.
+    fl = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    flx = torch.zeros(1, dtype=torch.int32, device="cuda")
+    fcall = Raw(mi, "mi_stream_read", fl, 4096, flx, st)
+    ts = _times_us(torch, lambda i: fcall(), iters)
+    print(json.dumps({"config": "launch_floor", "shape": "mi_stream_read over 4 KiB (one launch, "
+                      "no work to speak of): the per-call floor of this timing",
+                      "us_median": round(float(np.median(ts)), 2),
+                      "us_p10": round(float(np.percentile(ts, 10)), 2),
+                      "us_p90": round(float(np.percentile(ts, 90)), 2)}), flush=True)
+
     # 2. merge_state bf16 S=32768 H=32 D=128, inputs rotated over two copies
     c2 = inputs.merge_state_case(1002, S=32768, H=32, D=128, dtype="bf16")
     cp = [(to_dev(c2["va"], "bf16", torch), torch.from_numpy(c2["sa"]).cuda(),
