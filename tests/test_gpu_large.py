@@ -1,0 +1,151 @@
+"""Address arithmetic past 32 bits.
+
+The decode and cascade kernels must address K/V pages at any offset of the
+cache: the same small seeded case is run on its own caches and again with its
+pages moved past 4 GiB of a large cache (page ids shifted), and every output
+must be bit-identical, since only the addresses differ. The merge kernels must
+index tensors of more than 2^31 elements: a two-state merge and an N-state merge
+whose inputs cross that element count, checked against the oracle on the rows on
+both sides of it and at the start.
+"""
+import numpy as np
+import pytest
+import torch
+
+import lse_attention_state_amd as mi
+import oracle
+from lse_attention_state_amd import inputs
+from parity import check_lse, check_values, to_device
+
+pytestmark = pytest.mark.gpu
+
+# 32 KiB per page (8 kv heads x 16 tokens x 128 x 2 bytes): page ids from here
+# on start past 4 GiB of the cache.
+SHIFT = (1 << 32) // (8 * 16 * 128 * 2) + 3901
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _moved(cache: torch.Tensor) -> torch.Tensor:
+    big = torch.empty((SHIFT + cache.shape[0],) + tuple(cache.shape[1:]), dtype=cache.dtype,
+                      device=cache.device)
+    big[SHIFT:] = cache
+    return big
+
+
+def _shift(table: torch.Tensor) -> torch.Tensor:
+    return torch.where(table >= 0, table + SHIFT, table)
+
+
+def _same(a: torch.Tensor, b: torch.Tensor):
+    assert a.shape == b.shape and a.dtype == b.dtype
+    iv = torch.int16 if a.element_size() == 2 else torch.int32
+    assert torch.equal(a.view(iv), b.view(iv))
+
+
+def _release():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def test_decode_pages_past_4gib():
+    ctx = np.array([1000, 37, 4096, 300], np.int32)
+    _say("decode with pages past 4 GiB", ctx.tolist())
+    case = inputs.paged_kv_case(1201, ctx, 32, 8, 128, 16, dtype="f16")
+    q, k, v = (to_device(case[n], "f16") for n in ("q", "k", "v"))
+    pt = torch.from_numpy(case["page_table"]).cuda()
+    cl = torch.from_numpy(case["ctx_lens"]).cuda()
+    kb, vb, ptb = _moved(k), _moved(v), _shift(pt)
+    assert kb.numel() * kb.element_size() > (1 << 32) + (1 << 20)
+    sc = case["sm_scale"]
+    for splits in (1, 8):
+        a = mi.split_kv_decode(q, k, v, pt, cl, splits, sc, return_partials=True)
+        b = mi.split_kv_decode(q, kb, vb, ptb, cl, splits, sc, return_partials=True)
+        for x, y in zip(a, b):
+            _same(x, y)
+        a = mi.split_kv_decode_fused(q, k, v, pt, cl, splits, sc)
+        b = mi.split_kv_decode_fused(q, kb, vb, ptb, cl, splits, sc)
+        for x, y in zip(a, b):
+            _same(x, y)
+    indptr = mi.plan_splits_varlen(case["ctx_lens"], 8)
+    ip = torch.from_numpy(indptr).cuda()
+    a = mi.split_kv_decode_varlen(q, k, v, pt, cl, ip, sc)
+    b = mi.split_kv_decode_varlen(q, kb, vb, ptb, cl, ip, sc)
+    for x, y in zip(a, b):
+        _same(x, y)
+    o = torch.empty((4, 32, 128), dtype=torch.float16, device="cuda")
+    s = torch.empty((4, 32), dtype=torch.float32, device="cuda")
+    mi.split_kv_decode_noalloc(q, kb, vb, ptb, cl, 8, sc, o, s)
+    ref_o, ref_s = mi.split_kv_decode(q, k, v, pt, cl, 8, sc)
+    torch.cuda.synchronize()
+    _same(o, ref_o)
+    _same(s, ref_s)
+    # And the moved case against the oracle.
+    ro, rs = oracle.attention(case["q"], case["k"], case["v"], case["page_table"],
+                              case["ctx_lens"], sc, "f16", "f16")
+    check_values(b[0], ro)
+    check_lse(b[1], rs)
+    del kb, vb
+    _release()
+
+
+def test_cascade_pages_past_4gib():
+    _say("cascade with pages past 4 GiB")
+    cas = inputs.cascade_case(1202, R=8, prefix_len=1024, suffix_len=72)
+    q, k, v = (to_device(cas[n], "bf16") for n in ("q", "k", "v"))
+    pp = torch.from_numpy(cas["prefix_pages"]).cuda()
+    st = torch.from_numpy(cas["suffix_table"]).cuda()
+    sl = torch.from_numpy(cas["suffix_lens"]).cuda()
+    kb, vb = _moved(k), _moved(v)
+    a = mi.cascade_decode_fused(q, k, v, pp, cas["prefix_len"], st, sl, cas["sm_scale"])
+    b = mi.cascade_decode_fused(q, kb, vb, _shift(pp), cas["prefix_len"], _shift(st), sl,
+                                cas["sm_scale"])
+    for x, y in zip(a, b):
+        _same(x, y)
+    ro, rs = oracle.attention(cas["q"], cas["k"], cas["v"], cas["full_table"], cas["full_lens"],
+                              cas["sm_scale"], "bf16", "bf16")
+    check_values(b[0], ro)
+    check_lse(b[1], rs)
+    del kb, vb
+    _release()
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def test_merge_state_past_2g_elements():
+    rows = (1 << 24) + 64          # rows * 128 elements cross 2^31 at row 2^24
+    _say("merge_state over", rows, "rows of 128 bf16")
+    g = torch.Generator(device="cuda").manual_seed(1203)
+    va = torch.randn((rows, 128), generator=g, device="cuda").to(torch.bfloat16)
+    vb = torch.randn((rows, 128), generator=g, device="cuda").to(torch.bfloat16)
+    sa = torch.rand(rows, generator=g, device="cuda") * 40 - 20
+    sb = torch.rand(rows, generator=g, device="cuda") * 40 - 20
+    vo, so = mi.merge_state(va, sa, vb, sb)
+    torch.cuda.synchronize()
+    for r0, r1 in ((0, 32), ((1 << 24) - 32, rows)):
+        rv, rs = oracle.merge_state(_bits(va[r0:r1]), sa[r0:r1].cpu().numpy(),
+                                    _bits(vb[r0:r1]), sb[r0:r1].cpu().numpy(), "bf16")
+        check_values(vo[r0:r1], rv)
+        check_lse(so[r0:r1], rs)
+    del va, vb, vo
+    _release()
+
+
+def test_merge_states_past_2g_elements():
+    S, N = (1 << 22) + 32, 4       # (pos * N + n) * 128 crosses 2^31 at pos 2^22
+    _say("merge_states over", S, "positions x", N, "states of 128 f16")
+    g = torch.Generator(device="cuda").manual_seed(1204)
+    v = torch.randn((S, N, 1, 128), generator=g, device="cuda").to(torch.float16)
+    s = torch.rand((S, N, 1), generator=g, device="cuda") * 40 - 20
+    vo, so = mi.merge_states(v, s)
+    torch.cuda.synchronize()
+    for p0, p1 in ((0, 16), ((1 << 22) - 16, S)):
+        rv, rs = oracle.merge_states(_bits(v[p0:p1]), s[p0:p1].cpu().numpy(), "f16")
+        check_values(vo[p0:p1], rv)
+        check_lse(so[p0:p1], rs)
+    del v, vo
+    _release()
