@@ -1,4 +1,4 @@
-"""Address arithmetic past 32 bits.
+"""Address arithmetic past 32 bits, and the largest sizes.
 
 The decode and cascade kernels must address K/V pages at any offset of the
 cache: the same small seeded case is run on its own caches and again with its
@@ -6,7 +6,7 @@ pages moved past 4 GiB of a large cache (page ids shifted), and every output
 must be bit-identical, since only the addresses differ. The merge kernels must
 index tensors of more than 2^31 elements: a two-state merge and an N-state merge
 whose inputs cross that element count, checked against the oracle on the rows on
-both sides of it and at the start.
+both sides of it and at the start. And the decode at its largest batch.
 """
 import numpy as np
 import pytest
