@@ -180,3 +180,26 @@ def test_decode_largest_batch():
         check_values(o, ro)
         check_lse(s, rs)
     _release()
+
+
+@pytest.mark.parametrize("R,Hq,Hkv,prefix_len,dtype", [
+    (4, 4, 1, 65536, "bf16"),    # one row block, 512 chunks of 128 tokens
+    (2, 8, 8, 65552, "f16"),     # chunks at their 1024-token cap: 65 of them
+])
+def test_cascade_long_prefix(R, Hq, Hkv, prefix_len, dtype):
+    """A long shared prefix: many chunk states per row, merged by the suffix
+    kernel's combine from memory, or chunks at the cap of 64 pages."""
+    _say("cascade long prefix", R, Hq, Hkv, prefix_len, dtype)
+    cas = inputs.cascade_case(1206 + Hkv, R=R, prefix_len=prefix_len, suffix_len=40, Hq=Hq,
+                              Hkv=Hkv, dtype=dtype)
+    q, k, v = (to_device(cas[n], dtype) for n in ("q", "k", "v"))
+    pp = torch.from_numpy(cas["prefix_pages"]).cuda()
+    st = torch.from_numpy(cas["suffix_table"]).cuda()
+    sl = torch.from_numpy(cas["suffix_lens"]).cuda()
+    o, s = mi.cascade_decode_fused(q, k, v, pp, prefix_len, st, sl, cas["sm_scale"])
+    torch.cuda.synchronize()
+    ro, rs = oracle.attention(cas["q"], cas["k"], cas["v"], cas["full_table"], cas["full_lens"],
+                              cas["sm_scale"], dtype, dtype)
+    check_values(o, ro)
+    check_lse(s, rs)
+    _release()
