@@ -203,3 +203,25 @@ def test_cascade_long_prefix(R, Hq, Hkv, prefix_len, dtype):
     check_values(o, ro)
     check_lse(s, rs)
     _release()
+
+
+@pytest.mark.parametrize("dt_in", ["f32", "f16"])
+def test_merge_states_varlen_one_huge_set(dt_in):
+    """Index sets of 0-8 states with one set of 200,000 among them: the launch
+    sizes its lane teams for the short sets, so the long one is folded by one
+    team in batches; every row against the oracle."""
+    _say("varlen merge with one set of 200000 states", dt_in)
+    g = inputs.rng(1207)
+    lens = g.integers(0, 9, 3000)
+    lens[1234] = 200_000
+    indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    total, S, H, D = int(indptr[-1]), 3000, 2, 128
+    c = inputs.merge_states_case(1208, S=total, N=1, H=H, D=D, dtype=dt_in, s_lo=-30, s_hi=30)
+    v, s = np.ascontiguousarray(c["v"][:, 0]), np.ascontiguousarray(c["s"][:, 0])
+    vo, so = mi.merge_states_varlen(to_device(v, dt_in), torch.from_numpy(s).cuda(),
+                                    torch.from_numpy(indptr).cuda(), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rv, rs = oracle.merge_states_varlen(v, s, indptr, dt_in)
+    check_values(vo, rv)
+    check_lse(so, rs)
+    _release()
