@@ -188,8 +188,15 @@ __global__ __launch_bounds__(kBlock) void merge_states_kernel(
       for (int u = 0; u < kChunk; ++u) {
         const bool in = n0 + u * G < N;
         sv[u] = in ? sanitize_lse(sv[u]) : -kInf;
+        // A state past N gets weight 0 and the guarded FMA below skips it, so
+        // its clamped load (possibly NaN) never reaches acc; lanes past D are
+        // never stored. The zero-fill is therefore redundant: without it,
+        // chunks of 8 states run 10% faster (S=512 N=64 H=8 fp16: 16.2 ->
+        // 14.5 us); with 4 or fewer it measured 1-2% faster kept, so it stays.
+        if constexpr (kChunk < 8) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[u][j] = (in && lane_ok) ? x[u][j] : 0.0f;
+          for (int j = 0; j < 8; ++j) x[u][j] = (in && lane_ok) ? x[u][j] : 0.0f;
+        }
       }
       float cm = m;
 #pragma unroll
