@@ -8,29 +8,34 @@
 // block of 64 rows (one 16-row MFMA tile per wave) and one chunk of the
 // prefix, and runs an online softmax over the chunk in tiles of 32 tokens
 // (two pages). Two workgroups share a compute unit (two waves per SIMD), so
-// one wave's softmax arithmetic overlaps the other's matrix products. Everything is computed transposed, so that the softmax
-// weights never leave registers:
+// one wave's softmax arithmetic overlaps the other's matrix products.
+// Everything is computed transposed, so that the softmax weights never leave
+// registers:
 //   S^T = K Q^T    v_mfma_f32_16x16x32: A = K (16 tokens x 32 d) from LDS,
 //                  B = Q^T from registers; lane (l16, grp) receives the scores
 //                  of row l16 for tokens 4grp+e and 16+4grp+e (e < 4)
 //   P^T = 2^(S^T*scale*log2e - m), rounded to the input type: those eight
 //                  weights are exactly the lane's B operand of the next product
 //                  when its contraction slot grp holds those eight tokens
-//   O^T += V^T P^T v_mfma_f32_16x16x32: A = V^T (16 d x 32 tokens) from LDS,
-//                  stored transposed with the tokens of each slot adjacent
+//   O^T += V^T P^T v_mfma_f32_16x16x32: A = V^T (16 d x 32 tokens), read from
+//                  the row-major V tile with gfx950's transposing LDS read
+//                  (ds_read_b64_tr_b16: within each group of 16 lanes, lane j
+//                  receives element j%4 of the 8 bytes read by lanes j/4,
+//                  4+j/4, 8+j/4 and 12+j/4, so lanes that read 4 d values of
+//                  4 token rows hand each lane 4 tokens at one d)
 // The softmax denominator sums the fp32 weights, so the LSE is exact to fp32;
 // only the P V product uses the rounded weights. The running max of a row is
 // shared by the four lanes that hold it; it is raised only when a score passes
 // it by more than kRescaleSlack (rare after the first tile), which is when the
 // four lanes compare their maxima.
 //
-// LDS row strides are the ones measured free of bank conflicts on gfx950 for
-// this pattern (16 rows x 16 bytes per ds_read_b128): 288 bytes for K rows and
-// 96 bytes for V^T rows (272 and 80 bytes measured 1.7x slower, 256 bytes
-// 6.5x). The transposed V writes spread one instruction over all 16 token
-// pairs of a tile. Tiles are prefetched kDepth ahead in registers (K
-// through per-page buffer descriptors, V through per-lane global addresses); an
-// absent page contributes no tokens. Each workgroup writes its chunk's state
+// K and V tiles are both staged row-major with 288-byte rows, the stride
+// measured free of bank conflicts on gfx950 for the K reads (16 rows x 16
+// bytes per ds_read_b128; 272 bytes measured 1.7x slower, 256 bytes 6.5x).
+// (An earlier form staged V transposed with v_perm and scattered 4-byte
+// writes; the transposing read removes that work and runs 6% faster.)
+// Tiles are prefetched kDepth ahead in registers through per-page buffer
+// descriptors; an absent page reads as zeros and contributes no tokens. Each workgroup writes its chunk's state
 // (o, s) as fp32; the chunks are merged by the N-state merge kernel.
 #include "common.h"
 #include "launch.h"
@@ -45,7 +50,7 @@ constexpr int kBM = 4 * 16 * kRowTiles;    // query rows per workgroup
 constexpr int kBN = 32;                    // prefix tokens per tile
 constexpr int kThreads = 256;
 constexpr int kKStride = kD + 16;          // LDS row (elements) of the K tile: 288 bytes
-constexpr int kVtStride = kBN + 16;        // LDS row (elements) of the V^T tile: 96 bytes
+constexpr int kVStride = kD + 16;          // LDS row (elements) of the V tile: 288 bytes
 constexpr int kDepth = 2;                  // tiles in flight per thread (2 measured faster than 4 or 6)
 constexpr int kMaxChunkPages = 64;         // page ids of a chunk fit one VGPR of the wave
 constexpr int kBufferFlags = 0x00020000;
@@ -55,6 +60,9 @@ constexpr int kTargetBlocks = 512;        // two workgroups per compute unit
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 template <int DT>
 __device__ __forceinline__ f32x4_t mfma16x16x32(const u32x4_t& a, const u32x4_t& b,
@@ -73,11 +81,6 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   return DT == MI_BF16 ? pack_bf16(a, b) : pack_f16(a, b);
 }
 
-// Position of tile token t in a V^T row: contraction slot g = (t % 16) / 4
-// holds tokens 4g..4g+3 then 16+4g..16+4g+3, the order in which a lane of
-// group g holds its weights.
-__device__ __forceinline__ int vt_pos(int t) { return 8 * ((t & 15) >> 2) + 4 * (t >> 4) + (t & 3); }
-
 template <int DT>
 __global__ __launch_bounds__(kThreads, 2) void prefix_attention_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
@@ -85,7 +88,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefix_attention_kernel(
     int n_rows, int Hq, int Hkv, int G, int64_t num_phys, int chunk_tokens, int n_chunks,
     float qk_scale_log2, float* __restrict__ ws_o, float* __restrict__ ws_s) {
   __shared__ __attribute__((aligned(16))) uint16_t ks[2][kBN * kKStride];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[2][kD * kVtStride];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[2][kBN * kVStride];
 
   // Block -> (row block, kv head, chunk). The row blocks of one (kv head,
   // chunk) get ids that are equal modulo 8, so they run on one XCD and share
@@ -131,12 +134,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefix_attention_kernel(
       page0 + lane < n_pages && lane < 2 * n_tiles && ids >= 0 && ids < num_phys);
   auto page_ok = [&](int pl, int32_t) { return pl < 64 && ((ok_pages >> pl) & 1) != 0; };
 
-  // Staging roles. K: thread (p = tid/16, c = tid%16) takes tile tokens 2p,
-  // 2p+1 at d = 8c (its wave covers one page: p/8 = wave/2). V: thread
-  // (pv = tid%16, cv = tid/16) takes tokens 2pv, 2pv+1 at d = 8cv, so that one
-  // transposed-write instruction spreads over all 16 token pairs.
+  // Staging: thread (p = tid/16, c = tid%16) takes tile tokens 2p, 2p+1 at
+  // d = 8c of both K and V (its wave covers one page: p/8 = wave/2).
   const int kp = tid >> 4, kc8 = (tid & 15) * 8;
-  const int vp = tid & 15, vc8 = (tid >> 4) * 8;
   const int k_lane_bytes = ((2 * (kp & 7)) * kD + kc8) * 2;
   const int64_t tile_elems = static_cast<int64_t>(kPage) * kD;
   u32x4_t kbuf[kDepth][2], vbuf[kDepth][2];
@@ -153,43 +153,36 @@ __global__ __launch_bounds__(kThreads, 2) void prefix_attention_kernel(
       kbuf[j][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, k_lane_bytes, 0, 0));
       kbuf[j][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, k_lane_bytes + kD * 2, 0, 0));
     }
-    {  // V: the lane's page (its token pair's)
-      const int pl = 2 * t + (vp >> 3);
-      const int32_t phys0 = __builtin_amdgcn_readlane(ids, (2 * t) & 63);
-      const int32_t phys1 = __builtin_amdgcn_readlane(ids, (2 * t + 1) & 63);
-      const int32_t phys = (vp >> 3) ? phys1 : phys0;
+    {  // V: the wave's page, rows as for K
+      const int pl = 2 * t + (wave >> 1);
+      const int32_t phys = __builtin_amdgcn_readlane(ids, pl & 63);
       const bool ok = page_ok(pl, phys);
       vok[j] = ok;
-      vfull[j] = page_ok(2 * t, phys0) && page_ok(2 * t + 1, phys1) && tok0 + (t + 1) * kBN <= tok1;
-      const uint16_t* src = vc + (static_cast<int64_t>(ok ? phys : 0) * Hkv + hkv) * tile_elems +
-                            (2 * (vp & 7)) * kD + vc8;
-      vbuf[j][0] = *reinterpret_cast<const u32x4_t*>(src);
-      vbuf[j][1] = *reinterpret_cast<const u32x4_t*>(src + kD);
+      vfull[j] = page_ok(2 * t, __builtin_amdgcn_readlane(ids, (2 * t) & 63)) &&
+                 page_ok(2 * t + 1, __builtin_amdgcn_readlane(ids, (2 * t + 1) & 63)) &&
+                 tok0 + (t + 1) * kBN <= tok1;
+      const int64_t base = (static_cast<int64_t>(ok ? phys : 0) * Hkv + hkv) * tile_elems;
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(vc + base), 0, ok ? static_cast<int>(tile_elems * 2) : 0, kBufferFlags);
+      vbuf[j][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, k_lane_bytes, 0, 0));
+      vbuf[j][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, k_lane_bytes + kD * 2, 0, 0));
     }
   };
 
-  // Stage tile t (register slot j) into LDS buffer `buf`: K row-major, V
-  // transposed. V of tokens at or past the chunk end or on an absent page is
-  // written as zero (its scores are masked as well).
+  // Stage tile t (register slot j) into LDS buffer `buf`, K and V row-major.
+  // V of tokens at or past the chunk end or on an absent page is written as
+  // zero (their scores are masked as well, and 0 * NaN must not reach O).
   auto stage = [&](int t, int j, int buf) {
     *reinterpret_cast<u32x4_t*>(&ks[buf][(2 * kp) * kKStride + kc8]) = kbuf[j][0];
     *reinterpret_cast<u32x4_t*>(&ks[buf][(2 * kp + 1) * kKStride + kc8]) = kbuf[j][1];
     u32x4_t a = vbuf[j][0], b = vbuf[j][1];
-    if (!vfull[j]) {  // the chunk's last tile, or an absent page
+    if (!vfull[j]) {  // the chunk's last tile, or an absent page (already zeros)
       const int ttok = tok0 + t * kBN;
-      const bool v0 = vok[j] && ttok + 2 * vp < tok1;
-      const bool v1 = vok[j] && ttok + 2 * vp + 1 < tok1;
-      a = v0 ? a : u32x4_t{0, 0, 0, 0};
-      b = v1 ? b : u32x4_t{0, 0, 0, 0};
+      a = (vok[j] && ttok + 2 * kp < tok1) ? a : u32x4_t{0, 0, 0, 0};
+      b = (vok[j] && ttok + 2 * kp + 1 < tok1) ? b : u32x4_t{0, 0, 0, 0};
     }
-    uint32_t* vtw = reinterpret_cast<uint32_t*>(vt[buf]);
-    const int col = vt_pos(2 * vp) >> 1;  // dword column of the token pair
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // Low halves of the pair's two dwords, then high halves (v_perm_b32).
-      vtw[(vc8 + 2 * i) * (kVtStride / 2) + col] = __builtin_amdgcn_perm(b[i], a[i], 0x05040100u);
-      vtw[(vc8 + 2 * i + 1) * (kVtStride / 2) + col] = __builtin_amdgcn_perm(b[i], a[i], 0x07060302u);
-    }
+    *reinterpret_cast<u32x4_t*>(&vs[buf][(2 * kp) * kVStride + kc8]) = a;
+    *reinterpret_cast<u32x4_t*>(&vs[buf][(2 * kp + 1) * kVStride + kc8]) = b;
   };
 
   f32x4_t o[kRowTiles][8];
@@ -215,9 +208,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefix_attention_kernel(
     for (int r = 0; r < kRowTiles; ++r)
 #pragma unroll
       for (int c = 0; c < 2; ++c) s[r][c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    // All K operands are read before the products (one wave per SIMD has no
-    // other wave to hide LDS latency behind), likewise the V^T operands below,
-    // which are read before the softmax arithmetic.
+    // All K operands are read before the products, likewise the V^T operands
+    // below, which are read before the softmax arithmetic so that their LDS
+    // latency overlaps it.
     u32x4_t ka[4][2];
 #pragma unroll
     for (int k = 0; k < 4; ++k)
@@ -232,10 +225,23 @@ __global__ __launch_bounds__(kThreads, 2) void prefix_attention_kernel(
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int r = 0; r < kRowTiles; ++r) s[r][c] = mfma16x16x32<DT>(ka[k][c], qb[r][k], s[r][c]);
+    // V^T operand of d block c: lane (l16, grp) needs d = 16c + l16 at tokens
+    // 4grp..4grp+3 and 16+4grp..16+4grp+3; a transposing read in which lane s
+    // of each 16-lane group reads 4 d values of token row s/4 gives lane j the
+    // 4 token values at d column j.
     u32x4_t va[8];
+    const int tr_row = 4 * grp + (l16 >> 2);
+    const int tr_col = 4 * (l16 & 3);
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-      va[c] = *reinterpret_cast<const u32x4_t*>(&vt[buf][(16 * c + l16) * kVtStride + 8 * grp]);
+    for (int c = 0; c < 8; ++c) {
+      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4_t*)(&vs[buf][tr_row * kVStride + 16 * c + tr_col]));
+      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4_t*)(&vs[buf][(16 + tr_row) * kVStride + 16 * c + tr_col]));
+      const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo);
+      const u32x2_t h2 = __builtin_bit_cast(u32x2_t, hi);
+      va[c] = u32x4_t{l2.x, l2.y, h2.x, h2.y};
+    }
     __builtin_amdgcn_sched_barrier(0);
     // y = score * scale * log2(e) - mu, one FMA per score. Tokens at or past
     // the chunk end, or on an absent page, get y = -inf; only the chunk's last
