@@ -68,6 +68,41 @@ def test_prefix_attention_empty_prefix():
     assert torch.all(vo == 0) and torch.all(so == float("-inf"))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("R,Hq,Hkv,n_full,tail", [(5, 8, 2, 40, 7), (20, 16, 2, 300, 5)])
+def test_prefix_attention_absent_pages_and_nan_tail(dtype, R, Hq, Hkv, n_full, tail):
+    """Prefix page ids outside [0, pages) contribute no tokens, and whatever the
+    slots past the prefix end of its last page hold (NaN here, in K and V)
+    never reaches the result: equal to the oracle over the prefix with those
+    pages left out."""
+    _say("prefix absent pages / NaN tail", dtype, R, Hq, Hkv, n_full, tail)
+    prefix_len = 16 * n_full + tail
+    case = inputs.cascade_case(970 + R + n_full, R=R, prefix_len=16 * (n_full + 1), suffix_len=16,
+                               Hq=Hq, Hkv=Hkv, dtype=dtype)
+    nan_bits = 0x7FC0 if dtype == "bf16" else 0x7E00
+    last = case["prefix_pages"][n_full]
+    case["k"][last, :, tail:, :] = nan_bits
+    case["v"][last, :, tail:, :] = nan_bits
+    P = case["k"].shape[0]
+    absent = [3, n_full // 2]
+    pages_dev = case["prefix_pages"].copy()
+    pages_dev[absent[0]] = -1
+    pages_dev[absent[1]] = P
+    keep = np.array([i for i in range(n_full + 1) if i not in absent], np.int32)
+    q, k, v = _dev(case)
+    v_out = torch.full((R, Hq, 128), float("nan"), dtype=torch.float32, device="cuda")
+    s_out = torch.full((R, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    mi.prefix_attention(q, k, v, torch.from_numpy(pages_dev).cuda(), prefix_len, case["sm_scale"],
+                        v_out=v_out, s_out=s_out)
+    torch.cuda.synchronize()
+    table = np.ascontiguousarray(np.broadcast_to(case["prefix_pages"][keep], (R, len(keep))))
+    lens = np.full(R, prefix_len - 16 * len(absent), np.int32)
+    o, s = oracle.attention(case["q"], case["k"], case["v"], table, lens, case["sm_scale"],
+                            dtype, dtype)
+    check_values(v_out, o)
+    check_lse(s_out, s)
+
+
 def test_cascade_64_requests_8k_prefix_512_suffix():
     _say("cascade full")
     case = inputs.cascade_case(1005)
