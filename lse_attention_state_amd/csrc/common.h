@@ -149,10 +149,10 @@ __device__ __forceinline__ void unpack8_raw(const Raw8& r, float (&x)[8]) {
 }
 
 // Store of 8 elements rounded to DT. kStream: with the non-temporal hint, for
-// outputs a streaming merge writes once and does not read back (measured on
-// MI355X: the merges' dirty output no longer lingers in the last-level cache
-// to be written back during the next kernel, which made that kernel 7-8%
-// slower).
+// outputs a streaming kernel writes once and does not read back (measured on
+// MI355X for the two-state merge: its dirty output no longer lingers in the
+// last-level cache to be written back during the next kernel, which made that
+// kernel 7-8% slower). Which policy a kernel uses is measured per kernel.
 template <int DT, bool kStream = false>
 __device__ __forceinline__ void store8(void* base, int64_t off, const float (&x)[8]) {
   if constexpr (kStream) {

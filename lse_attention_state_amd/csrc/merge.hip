@@ -9,8 +9,18 @@
 // so every load instruction of a lane group covers one contiguous run). Every
 // load of a row or batch is issued before the first is used (scheduling
 // barriers keep the compiler from sinking loads toward their uses, which had
-// left one or two in flight). Inputs are loaded and outputs stored with the
-// non-temporal (streaming) hint.
+// left one or two in flight). Inputs are loaded with the non-temporal
+// (streaming) hint. Output stores, chosen per kernel by measurement on MI355X:
+//  - ordinary write-back stores in the N-state merge (fp16 S=65536 N=4 H=8
+//    D=128: 110.0 -> 101.9 us per call, and a step of the two merges, the B=1
+//    decode and the cascade 0.323 -> 0.316 ms) and wherever fp32 states are
+//    merged (the split-KV combines and both levels of the two-level merge,
+//    whose first level's output is read back at once: S=64 N=1024 13.4 ->
+//    12.5 us, S*H=1024 N=16 5.4 -> 4.2 us);
+//  - non-temporal stores in the two-state merge in all its modes and in the
+//    segmented merge of 16-bit states, where write-back measured slower (the
+//    bench step above 0.343 ms; sink in place 86 -> 94 us; mask all set 128 ->
+//    133 us; 65536 variable-length sets 114 -> 123 us).
 //
 // Empty-state handling: incoming s are sanitised (NaN, +inf -> -inf); weights
 // use the max-based guard so that -inf - (-inf) gives weight 0; a state of
@@ -54,13 +64,15 @@ __device__ __forceinline__ Raw8 load8_halves_raw(const float* row, int c, int ha
   return r;
 }
 
+// The output of a row merged from fp32 halves, in the same lane layout, with
+// write-back stores (see the file header).
 template <int DT>
 __device__ __forceinline__ void store8_halves(void* base, int64_t rowoff, int c, int half,
                                               const float (&x)[8]) {
   if constexpr (DT == MI_F32) {
     float* row = static_cast<float*>(base) + rowoff;
-    __builtin_nontemporal_store(float4_t{x[0], x[1], x[2], x[3]}, reinterpret_cast<float4_t*>(row + 4 * c));
-    __builtin_nontemporal_store(float4_t{x[4], x[5], x[6], x[7]}, reinterpret_cast<float4_t*>(row + half + 4 * c));
+    *reinterpret_cast<float4_t*>(row + 4 * c) = float4_t{x[0], x[1], x[2], x[3]};
+    *reinterpret_cast<float4_t*>(row + half + 4 * c) = float4_t{x[4], x[5], x[6], x[7]};
   } else {
     typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
     uint16_t* row = static_cast<uint16_t*>(base) + rowoff;
@@ -68,8 +80,8 @@ __device__ __forceinline__ void store8_halves(void* base, int64_t rowoff, int c,
                                       : u32x2_t{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
     const u32x2_t hi = (DT == MI_F16) ? u32x2_t{pack_f16(x[4], x[5]), pack_f16(x[6], x[7])}
                                       : u32x2_t{pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])};
-    __builtin_nontemporal_store(lo, reinterpret_cast<u32x2_t*>(row + 4 * c));
-    __builtin_nontemporal_store(hi, reinterpret_cast<u32x2_t*>(row + half + 4 * c));
+    *reinterpret_cast<u32x2_t*>(row + 4 * c) = lo;
+    *reinterpret_cast<u32x2_t*>(row + half + 4 * c) = hi;
   }
 }
 
@@ -251,7 +263,7 @@ __global__ __launch_bounds__(kBlock) void merge_states_kernel(
     if constexpr (kHalves)
       store8_halves<DTO>(vo, row * D, lane_in_row, D / 2, y);
     else
-      store8<DTO, true>(vo, row * D + d0, y);
+      store8<DTO, false>(vo, row * D + d0, y);  // write-back: see the file header
   }
   if (so != nullptr && lane_in_row == 0) so[row] = m + hw_log2(z);
 }
