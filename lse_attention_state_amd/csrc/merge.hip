@@ -10,17 +10,15 @@
 // load of a row or batch is issued before the first is used (scheduling
 // barriers keep the compiler from sinking loads toward their uses, which had
 // left one or two in flight). Inputs are loaded with the non-temporal
-// (streaming) hint. Output stores, chosen per kernel by measurement on MI355X:
-//  - ordinary write-back stores in the N-state merge (fp16 S=65536 N=4 H=8
-//    D=128: 110.0 -> 101.9 us per call, and a step of the two merges, the B=1
-//    decode and the cascade 0.323 -> 0.316 ms) and wherever fp32 states are
-//    merged (the split-KV combines and both levels of the two-level merge,
-//    whose first level's output is read back at once: S=64 N=1024 13.4 ->
-//    12.5 us, S*H=1024 N=16 5.4 -> 4.2 us);
-//  - non-temporal stores in the two-state merge in all its modes and in the
-//    segmented merge of 16-bit states, where write-back measured slower (the
-//    bench step above 0.343 ms; sink in place 86 -> 94 us; mask all set 128 ->
-//    133 us; 65536 variable-length sets 114 -> 123 us).
+// (streaming) hint. Output stores: non-temporal, except where fp32 states are
+// merged (the split-KV combines and both levels of the two-level merge), whose
+// outputs are small or read back at once by the next level; there ordinary
+// write-back stores measured faster on MI355X (S=64 N=1024 two-level merge
+// 13.4 -> 12.5 us, S*H=1024 N=16 5.4 -> 4.2 us). For the large 16-bit streams
+// write-back stores only looked faster while one output buffer was rewritten
+// call after call (the Infinity Cache absorbed the rewrites); with the output
+// rotated over four buffers they were slower (N-state merge fp16 S=65536 N=4
+// H=8: 110.8 -> 114.8 us), and in the two-state merge slower in every mode.
 //
 // Empty-state handling: incoming s are sanitised (NaN, +inf -> -inf); weights
 // use the max-based guard so that -inf - (-inf) gives weight 0; a state of
@@ -263,7 +261,7 @@ __global__ __launch_bounds__(kBlock) void merge_states_kernel(
     if constexpr (kHalves)
       store8_halves<DTO>(vo, row * D, lane_in_row, D / 2, y);
     else
-      store8<DTO, false>(vo, row * D + d0, y);  // write-back: see the file header
+      store8<DTO, true>(vo, row * D + d0, y);
   }
   if (so != nullptr && lane_in_row == 0) so[row] = m + hw_log2(z);
 }
