@@ -48,7 +48,8 @@ typedef enum {
   MI_ERR_NULL = 1,        /* a required pointer is NULL */
   MI_ERR_SHAPE = 2,       /* a size is negative/zero where it must be positive, or inconsistent */
   MI_ERR_DTYPE = 3,       /* dtype code out of range or not allowed for this argument */
-  MI_ERR_UNSUPPORTED = 4, /* valid but not built: head dim, page size, group size, alignment */
+  MI_ERR_UNSUPPORTED = 4, /* valid but not built: head dim, page size, group size, alignment,
+                             or a launch past 2^32 work-items */
   MI_ERR_HIP = 5,         /* a HIP launch failed */
   MI_ERR_ALIAS = 6,       /* outputs overlap inputs other than by exact in-place aliasing */
   MI_ERR_SCRATCH = 7      /* the work needs more than the library's static scratch holds */

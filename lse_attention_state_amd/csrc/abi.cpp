@@ -37,7 +37,12 @@ bool bad_alias(const void* out, int64_t out_bytes, const void* in, int64_t in_by
   return !(exact_ok && out == in && out_bytes == in_bytes);
 }
 
-mi_status from_hip(hipError_t e) { return e == hipSuccess ? MI_OK : MI_ERR_HIP; }
+// hipErrorInvalidConfiguration comes from a launcher's own check that the grid
+// fits (nothing was launched): a size the library does not support.
+mi_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return MI_OK;
+  return e == hipErrorInvalidConfiguration ? MI_ERR_UNSUPPORTED : MI_ERR_HIP;
+}
 
 // Compute units of the current device, cached per device (the only state the
 // library keeps; concurrent first calls store the same value).
@@ -315,7 +320,7 @@ mi_status mi_split_kv_decode(const void* q, const void* k_cache, const void* v_c
   hipError_t e = mi::launch_split_kv_partial(q, k_cache, v_cache, page_table, pt_stride, ctx_lens,
                                              B, Hq, Hkv, num_phys_pages, num_splits, sm_scale,
                                              kv_dtype, o_part, lse_part, s);
-  if (e != hipSuccess) return MI_ERR_HIP;
+  if (e != hipSuccess) return from_hip(e);
   // The combine: o_part [B, Hq, splits, D] is merge_states' [S = B*Hq, N = splits, H = 1, D].
   return from_hip(mi::launch_merge_states(o_part, lse_part, o, lse, int64_t(B) * Hq, num_splits,
                                           1, D, MI_F32, out_dtype, s));
@@ -345,7 +350,7 @@ mi_status mi_split_kv_decode_fused(const void* q, const void* k_cache, const voi
     hipError_t e = mi::launch_split_kv_partial(q, k_cache, v_cache, page_table, pt_stride,
                                                ctx_lens, B, Hq, Hkv, num_phys_pages, num_splits,
                                                sm_scale, kv_dtype, o_part, lse_part, hs);
-    if (e != hipSuccess) return MI_ERR_HIP;
+    if (e != hipSuccess) return from_hip(e);
     return from_hip(mi::launch_merge_states(o_part, lse_part, o, lse, int64_t(B) * Hq, num_splits,
                                             1, D, MI_F32, out_dtype, hs));
   }

@@ -386,7 +386,9 @@ hipError_t launch_prefix_chunks(const void* q, const void* kc, const void* vc,
   const int G = Hq / Hkv;
   const int n_rows = R * G;
   const int n_rb = (n_rows + kBM - 1) / kBM;
-  const dim3 grid(static_cast<unsigned>(n_rb * Hkv * n_chunks));
+  const int64_t blocks = int64_t(n_rb) * Hkv * n_chunks;
+  if (!grid_fits(blocks, kThreads)) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<unsigned>(blocks));
   const float scale = static_cast<float>(static_cast<double>(sm_scale) * 1.4426950408889634);
   const uint16_t* q16 = static_cast<const uint16_t*>(q);
   const uint16_t* k16 = static_cast<const uint16_t*>(kc);

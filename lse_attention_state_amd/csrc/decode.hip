@@ -905,9 +905,7 @@ hipError_t launch_dtype(int out_dtype, int G, unsigned blocks, hipStream_t st, c
 }
 
 // Workgroups for `items` work items of each of Hkv kv heads.
-unsigned decode_blocks(int64_t items, int Hkv) {
-  return static_cast<unsigned>(items * Hkv);
-}
+int64_t decode_blocks(int64_t items, int Hkv) { return items * Hkv; }
 
 }  // namespace
 
@@ -921,7 +919,9 @@ hipError_t launch_split_kv_partial(const void* q, const void* kc, const void* vc
                                    int prior_n) {
   const int G = Hq / Hkv;
   const int64_t items = static_cast<int64_t>(B) * num_splits;
-  const unsigned blocks = decode_blocks(items, Hkv);
+  const int64_t nblocks = decode_blocks(items, Hkv);
+  if (!grid_fits(nblocks, kThreads)) return hipErrorInvalidConfiguration;
+  const unsigned blocks = static_cast<unsigned>(nblocks);
   const float scale = static_cast<float>(static_cast<double>(sm_scale) * 1.4426950408889634);
   // o is written by this kernel when fused (counters given) or when there is a
   // single split (no combine needed); otherwise pass 1 only.
@@ -945,7 +945,9 @@ hipError_t launch_split_kv_partial_varlen(const void* q, const void* kc, const v
                                           float* o_part, float* lse_part, hipStream_t st,
                                           int32_t* counters, void* o, float* lse, int out_dtype) {
   const int G = Hq / Hkv;
-  const unsigned blocks = decode_blocks(total_splits, Hkv);
+  const int64_t nblocks = decode_blocks(total_splits, Hkv);
+  if (!grid_fits(nblocks, kThreads)) return hipErrorInvalidConfiguration;
+  const unsigned blocks = static_cast<unsigned>(nblocks);
   const float scale = static_cast<float>(static_cast<double>(sm_scale) * 1.4426950408889634);
   const int dto = counters != nullptr ? out_dtype : -1;
   if (kv_dtype == MI_F16)

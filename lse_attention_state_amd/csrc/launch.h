@@ -6,6 +6,14 @@
 
 namespace mi {
 
+// A 1-D launch of `blocks` workgroups of `threads` lanes fits HIP's grid,
+// whose size is counted in work-items in 32 bits. Launchers check this before
+// launching and return hipErrorInvalidConfiguration otherwise (the C ABI
+// reports MI_ERR_UNSUPPORTED), so a grid never wraps.
+inline bool grid_fits(int64_t blocks, int threads) {
+  return blocks >= 0 && blocks <= int64_t(0xFFFFFFFF) / threads;
+}
+
 hipError_t launch_merge_state(const void* va, const float* sa, const void* vb, const float* sb,
                               void* vo, float* so, int64_t rows, int D, int dt_in, int dt_out,
                               hipStream_t stream);

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4_t* __
 hipError_t launch_stream_read(const void* x, int64_t bytes, uint32_t* xor_out, hipStream_t st) {
   const int64_t n16 = bytes / 16;
   const int64_t blocks = (n16 + kThreads * kUnroll - 1) / (kThreads * kUnroll);
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (!grid_fits(blocks, kThreads)) return hipErrorInvalidConfiguration;
   stream_read_kernel<<<dim3(static_cast<unsigned>(blocks)), kThreads, 0, st>>>(
       static_cast<const u32x4_t*>(x), n16, xor_out);
   return hipGetLastError();

@@ -291,7 +291,9 @@ hipError_t merge_state_mode(const void* va, const float* sa, const void* vb, con
                             const uint8_t* mask, const float* sink, int H, hipStream_t st) {
   const int lanes_shift = log2_int(next_pow2(D / 8));
   const int64_t rows_per_block = kBlock >> lanes_shift;
-  const dim3 grid(static_cast<unsigned>((rows + rows_per_block - 1) / rows_per_block));
+  const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
+  if (!grid_fits(blocks, kBlock)) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<unsigned>(blocks));
   switch (dt_in) {
     case MI_F16: return merge_state_out<MI_F16, MODE>(dt_out, va, sa, vb, sb, vo, so, rows, D, lanes_shift, mask, sink, H, grid, st);
     case MI_BF16: return merge_state_out<MI_BF16, MODE>(dt_out, va, sa, vb, sb, vo, so, rows, D, lanes_shift, mask, sink, H, grid, st);
@@ -512,7 +514,9 @@ hipError_t merge_segments_k(int K, int64_t rows, hipStream_t st, const void* v, 
                             int H, int D, int lanes_shift, int team_shift, int parts) {
   const int threads = team_shift > 8 ? 1024 : 256;
   const int64_t rows_per_block = threads >> team_shift;
-  const dim3 grid(static_cast<unsigned>((rows + rows_per_block - 1) / rows_per_block));
+  const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
+  if (!grid_fits(blocks, threads)) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<unsigned>(blocks));
   if constexpr (DTI == MI_F32) {
     if (D == (8 << lanes_shift)) {
       if (threads == 1024)
@@ -687,7 +691,9 @@ hipError_t launch_merge_states(const void* v, const float* s, void* vo, float* s
   const int per_group = (N + G - 1) / G;
   const int chunk = per_group >= 8 ? 8 : next_pow2(per_group);
   const int64_t rows_per_block = kBlock >> (lanes_shift + groups_shift);
-  const dim3 grid(static_cast<unsigned>((rows + rows_per_block - 1) / rows_per_block));
+  const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
+  if (!grid_fits(blocks, kBlock)) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<unsigned>(blocks));
   switch (dt_in) {
     case MI_F16: return merge_states_out<MI_F16>(dt_out, chunk, v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift, grid, st);
     case MI_BF16: return merge_states_out<MI_BF16>(dt_out, chunk, v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift, grid, st);

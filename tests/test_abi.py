@@ -168,6 +168,18 @@ def test_decode_validation(fn):
     assert _dec(fn, B=0) == OK                # nothing to do, nothing launched
 
 
+def test_launch_grid_limit_is_refused():
+    """Sizes the argument checks accept but whose 1-D launch would exceed HIP's
+    2^32 work-items are refused with MI_ERR_UNSUPPORTED before any launch (the
+    grid is never truncated): split-KV pass 1 with 65535 x 1024 x 64 work
+    items, and a two-state merge of 2^28 rows."""
+    big = dict(B=65535, splits=1024, Hq=64, Hkv=64, op=P(1 << 50), lp=P(1 << 53))
+    assert _dec("mi_split_kv_partial", **big) == EUNSUP
+    assert _dec("mi_split_kv_decode", **big) == EUNSUP
+    assert _ms(S=1 << 28, H=1, va=P(0), sa=P(1 << 37), vb=P(2 << 37), sb=P(3 << 37),
+               vo=P(4 << 37), so=P(5 << 37)) == EUNSUP
+
+
 def test_decode_output_validation():
     assert _dec(o=NULL) == ENULL
     assert _dec(dto=9) == EDTYPE
