@@ -11,10 +11,10 @@
 // barriers keep the compiler from sinking loads toward their uses, which had
 // left one or two in flight). Inputs are loaded with the non-temporal
 // (streaming) hint. Output stores: non-temporal, except where fp32 states are
-// merged (the split-KV combines and both levels of the two-level merge), whose
-// outputs are small or read back at once by the next level; there ordinary
-// write-back stores measured faster on MI355X (S=64 N=1024 two-level merge
-// 13.4 -> 12.5 us, S*H=1024 N=16 5.4 -> 4.2 us). For the large 16-bit streams
+// merged (the split-KV combines and both levels of the two-level merge) into an
+// output of at most 64 MiB, small or read back at once by the next level;
+// there ordinary write-back stores measured faster on MI355X (S=64 N=1024
+// two-level merge 13.4 -> 12.5 us, S*H=1024 N=16 5.4 -> 4.2 us). For large streams
 // write-back stores only looked faster while one output buffer was rewritten
 // call after call (the Infinity Cache absorbed the rewrites); with the output
 // rotated over four buffers they were slower (N-state merge fp16 S=65536 N=4
@@ -62,15 +62,22 @@ __device__ __forceinline__ Raw8 load8_halves_raw(const float* row, int c, int ha
   return r;
 }
 
-// The output of a row merged from fp32 halves, in the same lane layout, with
-// write-back stores (see the file header).
+// The output of a row merged from fp32 halves, in the same lane layout:
+// write-back stores when `wb` (a small output, see the file header), else
+// non-temporal ones.
 template <int DT>
 __device__ __forceinline__ void store8_halves(void* base, int64_t rowoff, int c, int half,
-                                              const float (&x)[8]) {
+                                              const float (&x)[8], bool wb) {
   if constexpr (DT == MI_F32) {
     float* row = static_cast<float*>(base) + rowoff;
-    *reinterpret_cast<float4_t*>(row + 4 * c) = float4_t{x[0], x[1], x[2], x[3]};
-    *reinterpret_cast<float4_t*>(row + half + 4 * c) = float4_t{x[4], x[5], x[6], x[7]};
+    const float4_t a{x[0], x[1], x[2], x[3]}, b{x[4], x[5], x[6], x[7]};
+    if (wb) {
+      *reinterpret_cast<float4_t*>(row + 4 * c) = a;
+      *reinterpret_cast<float4_t*>(row + half + 4 * c) = b;
+    } else {
+      __builtin_nontemporal_store(a, reinterpret_cast<float4_t*>(row + 4 * c));
+      __builtin_nontemporal_store(b, reinterpret_cast<float4_t*>(row + half + 4 * c));
+    }
   } else {
     typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
     uint16_t* row = static_cast<uint16_t*>(base) + rowoff;
@@ -78,10 +85,18 @@ __device__ __forceinline__ void store8_halves(void* base, int64_t rowoff, int c,
                                       : u32x2_t{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
     const u32x2_t hi = (DT == MI_F16) ? u32x2_t{pack_f16(x[4], x[5]), pack_f16(x[6], x[7])}
                                       : u32x2_t{pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])};
-    *reinterpret_cast<u32x2_t*>(row + 4 * c) = lo;
-    *reinterpret_cast<u32x2_t*>(row + half + 4 * c) = hi;
+    if (wb) {
+      *reinterpret_cast<u32x2_t*>(row + 4 * c) = lo;
+      *reinterpret_cast<u32x2_t*>(row + half + 4 * c) = hi;
+    } else {
+      __builtin_nontemporal_store(lo, reinterpret_cast<u32x2_t*>(row + 4 * c));
+      __builtin_nontemporal_store(hi, reinterpret_cast<u32x2_t*>(row + half + 4 * c));
+    }
   }
 }
+
+// Outputs up to this size take write-back stores in the fp32-state merges.
+constexpr int64_t kWriteBackMaxBytes = int64_t(64) << 20;
 
 // Two states. Lanes per row L = 2^lanes_shift >= D/8; a block covers 256/L rows.
 // MODE: kPlain; kMasked (mask [rows / H] bytes, 0 = keep state a untouched);
@@ -150,7 +165,7 @@ template <int DTI, int DTO, int kChunk, bool kHalves = false>
 __global__ __launch_bounds__(kBlock) void merge_states_kernel(
     const void* __restrict__ v, const float* __restrict__ s, void* __restrict__ vo,
     float* __restrict__ so, int64_t rows, int N, int H, int D, int lanes_shift,
-    int groups_shift) {
+    int groups_shift, int wb) {
   __shared__ float lds[kLdsFloats];
   const int L = 1 << lanes_shift;
   const int G = 1 << groups_shift;
@@ -259,7 +274,7 @@ __global__ __launch_bounds__(kBlock) void merge_states_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) y[j] = acc[j] * inv;
     if constexpr (kHalves)
-      store8_halves<DTO>(vo, row * D, lane_in_row, D / 2, y);
+      store8_halves<DTO>(vo, row * D, lane_in_row, D / 2, y, wb != 0);
     else
       store8<DTO, true>(vo, row * D + d0, y);
   }
@@ -324,7 +339,7 @@ template <int DTI, int DTO, int K, int kSegThreads, bool kHalves = false>
 __global__ __launch_bounds__(kSegThreads) void merge_segments_kernel(
     const void* __restrict__ v, const float* __restrict__ s, const int32_t* __restrict__ indptr,
     int64_t total, int N, void* __restrict__ vo, float* __restrict__ so, int64_t rows, int H,
-    int D, int lanes_shift, int team_shift, int parts) {
+    int D, int lanes_shift, int team_shift, int parts, int wb) {
   __shared__ float lds_acc[kSegThreads / 64][kSegMaxD];
   __shared__ float lds_mz[kSegThreads / 64][2];
   const int L = 1 << lanes_shift;
@@ -478,7 +493,7 @@ __global__ __launch_bounds__(kSegThreads) void merge_segments_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) y[j] = acc[j] * inv;
     if constexpr (kHalves)
-      store8_halves<DTO>(vo, row * D, c, D / 2, y);
+      store8_halves<DTO>(vo, row * D, c, D / 2, y, wb != 0);
     else
       store8<DTO, true>(vo, row * D + d0, y);
   }
@@ -489,19 +504,19 @@ template <int DTI, int DTO, int kThr, bool kH = false>
 hipError_t merge_segments_kt(int K, dim3 grid, hipStream_t st, const void* v, const float* s,
                              const int32_t* indptr, int64_t total, int N, void* vo, float* so,
                              int64_t rows, int H, int D, int lanes_shift, int team_shift,
-                             int parts) {
+                             int parts, int wb) {
   switch (K) {
     case 1:
-      merge_segments_kernel<DTI, DTO, 1, kThr, kH><<<grid, kThr, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts);
+      merge_segments_kernel<DTI, DTO, 1, kThr, kH><<<grid, kThr, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts, wb);
       break;
     case 2:
-      merge_segments_kernel<DTI, DTO, 2, kThr, kH><<<grid, kThr, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts);
+      merge_segments_kernel<DTI, DTO, 2, kThr, kH><<<grid, kThr, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts, wb);
       break;
     case 4:
-      merge_segments_kernel<DTI, DTO, 4, kThr, kH><<<grid, kThr, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts);
+      merge_segments_kernel<DTI, DTO, 4, kThr, kH><<<grid, kThr, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts, wb);
       break;
     default:
-      merge_segments_kernel<DTI, DTO, 8, kThr, kH><<<grid, kThr, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts);
+      merge_segments_kernel<DTI, DTO, 8, kThr, kH><<<grid, kThr, 0, st>>>(v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts, wb);
       break;
   }
   return hipGetLastError();
@@ -517,16 +532,17 @@ hipError_t merge_segments_k(int K, int64_t rows, hipStream_t st, const void* v, 
   const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
   if (!grid_fits(blocks, threads)) return hipErrorInvalidConfiguration;
   const dim3 grid(static_cast<unsigned>(blocks));
+  const int wb = rows * D * (DTO == MI_F32 ? 4 : 2) <= kWriteBackMaxBytes;
   if constexpr (DTI == MI_F32) {
     if (D == (8 << lanes_shift)) {
       if (threads == 1024)
-        return merge_segments_kt<DTI, DTO, 1024, true>(K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts);
-      return merge_segments_kt<DTI, DTO, 256, true>(K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts);
+        return merge_segments_kt<DTI, DTO, 1024, true>(K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts, wb);
+      return merge_segments_kt<DTI, DTO, 256, true>(K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts, wb);
     }
   }
   if (threads == 1024)
-    return merge_segments_kt<DTI, DTO, 1024>(K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts);
-  return merge_segments_kt<DTI, DTO, 256>(K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts);
+    return merge_segments_kt<DTI, DTO, 1024>(K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts, wb);
+  return merge_segments_kt<DTI, DTO, 256>(K, grid, st, v, s, indptr, total, N, vo, so, rows, H, D, lanes_shift, team_shift, parts, wb);
 }
 
 template <int DTI>
@@ -548,18 +564,19 @@ template <int DTI, int DTO, bool kH>
 hipError_t merge_states_chunk(int chunk, const void* v, const float* s, void* vo, float* so,
                               int64_t rows, int N, int H, int D, int lanes_shift,
                               int groups_shift, dim3 grid, hipStream_t st) {
+  const int wb = rows * D * (DTO == MI_F32 ? 4 : 2) <= kWriteBackMaxBytes;
   switch (chunk) {
     case 1:
-      merge_states_kernel<DTI, DTO, 1, kH><<<grid, kBlock, 0, st>>>(v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift);
+      merge_states_kernel<DTI, DTO, 1, kH><<<grid, kBlock, 0, st>>>(v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift, wb);
       break;
     case 2:
-      merge_states_kernel<DTI, DTO, 2, kH><<<grid, kBlock, 0, st>>>(v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift);
+      merge_states_kernel<DTI, DTO, 2, kH><<<grid, kBlock, 0, st>>>(v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift, wb);
       break;
     case 4:
-      merge_states_kernel<DTI, DTO, 4, kH><<<grid, kBlock, 0, st>>>(v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift);
+      merge_states_kernel<DTI, DTO, 4, kH><<<grid, kBlock, 0, st>>>(v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift, wb);
       break;
     default:
-      merge_states_kernel<DTI, DTO, 8, kH><<<grid, kBlock, 0, st>>>(v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift);
+      merge_states_kernel<DTI, DTO, 8, kH><<<grid, kBlock, 0, st>>>(v, s, vo, so, rows, N, H, D, lanes_shift, groups_shift, wb);
       break;
   }
   return hipGetLastError();
